@@ -1,0 +1,105 @@
+"""Seeded synthetic inputs for the linear recurrence and the S6 selective scan.
+
+This module only draws random numbers and lays them out; it holds none of the
+scan's arithmetic. Both the float64 oracle tests and the GPU tests/bench take
+their inputs from here, so the two sides see bit-identical data.
+
+Distributions follow the workloads the pages describe:
+
+* linear recurrence h[t] = a[t] h[t-1] + b[t] ("Selective-scan CUDA kernels",
+  the paragraph that states the recurrence): ``a ~ U(lo, hi)``, ``b ~ N(0, 1)``,
+  fp32, one sequence.
+* S6 forward (POPCORNBENCH transcript FW-GLM-5-1, level 2 problem 30: the
+  problem statement's forward pass): ``u ~ N(0,1)``,
+  ``delta = softplus(N(-1, 0.5))`` (0.5 is the standard deviation),
+  ``A[d, n] = -exp(log(n + 1)) = -(n + 1)`` for every channel d,
+  ``B, C ~ N(0, 1)`` of shape (batch, L, N), ``D = 1``.
+  u, delta, B, C are fp32 or bf16 (rounded to nearest even from the fp32/f64
+  draw); A and D stay fp32.
+
+All draws use a CPU ``torch.Generator`` seeded with the given seed, in the
+fixed order documented in each function.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+# Named workloads. Sizes are those of the pages' problem (batch 16, d 256,
+# N 16 for the short S6 case) and of the long/bidirectional variants.
+LINEAR_WORKLOADS = {
+    "linear-n65536": dict(n=65536, a_lo=0.9, a_hi=1.0, seed=1001),
+    "linear-n134217728": dict(n=1 << 27, a_lo=0.5, a_hi=1.0, seed=1002),
+}
+
+S6_WORKLOADS = {
+    "s6-fwd-b16-L1024-d256-N16-f32": dict(
+        batch=16, L=1024, d_inner=256, N=16, dtype="f32", direction="fwd", seed=1003),
+    "s6-fwd-b1-L65536-d1024-N16-bf16": dict(
+        batch=1, L=65536, d_inner=1024, N=16, dtype="bf16", direction="fwd", seed=1004),
+    "s6-bidir-b4-L8192-d1536-N16-bf16": dict(
+        batch=4, L=8192, d_inner=1536, N=16, dtype="bf16", direction="bidir", seed=1005),
+}
+
+
+def linear_inputs(n: int, seed: int, a_lo: float = 0.5, a_hi: float = 1.0):
+    """Return fp32 CPU tensors (a, b) of length n.
+
+    Draw order: a (uniform on [a_lo, a_hi)), then b (standard normal).
+    """
+    g = torch.Generator().manual_seed(seed)
+    a = torch.rand(n, generator=g, dtype=torch.float32) * (a_hi - a_lo) + a_lo
+    b = torch.randn(n, generator=g, dtype=torch.float32)
+    return a, b
+
+
+@dataclass
+class S6Inputs:
+    u: torch.Tensor      # (batch, L, d_inner), fp32 or bf16
+    delta: torch.Tensor  # (batch, L, d_inner), fp32 or bf16, already > 0
+    A: torch.Tensor      # (d_inner, N) fp32
+    B: torch.Tensor      # (batch, L, N), fp32 or bf16
+    C: torch.Tensor      # (batch, L, N), fp32 or bf16
+    D: torch.Tensor      # (d_inner,) fp32
+
+    def as_f64(self):
+        """The same values widened to float64 (exact for fp32 and bf16)."""
+        return tuple(t.to(torch.float64).numpy() for t in
+                     (self.u, self.delta, self.A, self.B, self.C, self.D))
+
+
+def s6_inputs(batch: int, L: int, d_inner: int, N: int, seed: int,
+              dtype: str = "f32") -> S6Inputs:
+    """Draw one S6 problem on the CPU.
+
+    Draw order: u, the pre-activation of delta, B, C (all standard normal;
+    delta's pre-activation is then scaled to std 0.5 and shifted to mean -1).
+    delta = log1p(exp(x)) is evaluated in float64 and rounded once to the
+    storage dtype.
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    g = torch.Generator().manual_seed(seed)
+    u = torch.randn(batch, L, d_inner, generator=g, dtype=torch.float32)
+    x = torch.randn(batch, L, d_inner, generator=g, dtype=torch.float32)
+    x = x.to(torch.float64) * 0.5 - 1.0
+    delta = torch.log1p(torch.exp(x))
+    B = torch.randn(batch, L, N, generator=g, dtype=torch.float32)
+    C = torch.randn(batch, L, N, generator=g, dtype=torch.float32)
+    A = -torch.arange(1, N + 1, dtype=torch.float64).log().exp()
+    A = A.to(torch.float32).expand(d_inner, N).contiguous()
+    D = torch.ones(d_inner, dtype=torch.float32)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    return S6Inputs(u=u.to(tdt), delta=delta.to(tdt), A=A, B=B.to(tdt),
+                    C=C.to(tdt), D=D)
+
+
+def s6_workload_inputs(name: str) -> S6Inputs:
+    w = S6_WORKLOADS[name]
+    return s6_inputs(w["batch"], w["L"], w["d_inner"], w["N"], w["seed"], w["dtype"])
+
+
+def linear_workload_inputs(name: str):
+    w = LINEAR_WORKLOADS[name]
+    return linear_inputs(w["n"], w["seed"], w["a_lo"], w["a_hi"])
