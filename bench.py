@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the affine-recurrence look-back scan (and, as secondary lines
+of the same record, the S6 selective scan) on one MI355X.
+
+A step is one pass of the linear recurrence h[t] = a[t] h[t-1] + b[t] over a
+single fp32 sequence of n = 2^27 elements (a ~ U(0.5, 1), b ~ N(0, 1), h0 = 0),
+inputs resident in HBM. `value` is elements per second over the timed steps.
+The S6 workloads (forward fp32 16x1024x256, forward bf16 1x65536x1024,
+bidirectional bf16 4x8192x1536, N = 16) are timed the same way and reported
+under "s6". Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+CUS, CLOCK_GHZ, LANES = 256, 2.4, 64
+VALU_PEAK_T = CUS * LANES * CLOCK_GHZ / 1e3   # 39.32 T lane-instructions/s (fp32, unpacked)
+LINEAR_WORKLOAD = "linear-n134217728"
+LINEAR_BYTES_PER_ELEM = 12     # read a, b; write h (fp32)
+PROFILES = ROOT / "profiles"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        h.update((ROOT / "mamba_s6_selective_amd" / "csrc" / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kind, kernel_src):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or
+    None if absent or taken on a different kernel source."""
+    f = PROFILES / f"{kind}_traffic.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    if d.get("kernel_source_sha") != source_hash(kernel_src):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def time_steps(fn, steps, warmup):
+    """Runs fn() warmup times, then `steps` timed times with one HIP event pair
+    per step on torch's current stream (where the library launches)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in ev]
+    return wall * 1e3 / steps, statistics.mean(per), min(per)
+
+
+def sentinel_ok(dev):
+    import torch
+    import mamba_s6_selective_amd as ssm
+    x = torch.arange(1 << 22, dtype=torch.float32, device=dev) * 0.5 - 7.0
+    y = torch.empty_like(x)
+    ssm.copy_f32(x, y)
+    torch.cuda.synchronize()
+    return bool(torch.equal(x, y))
+
+
+def bench_linear(dev, steps, warmup):
+    import torch
+    import mamba_s6_selective_amd as ssm
+    from mamba_s6_selective_amd.workloads import LINEAR_WORKLOADS, linear_workload_inputs
+    n = LINEAR_WORKLOADS[LINEAR_WORKLOAD]["n"]
+    a, b = linear_workload_inputs(LINEAR_WORKLOAD)
+    a, b = a.to(dev), b.to(dev)
+    h = torch.empty_like(a)
+    ms_step, ms_kernel, ms_min = time_steps(lambda: ssm.linear_scan(a, b, 0.0, out=h),
+                                            steps, warmup)
+    return n, ms_step, ms_kernel, ms_min
+
+
+def bench_copy(dev, steps, warmup):
+    import torch
+    import mamba_s6_selective_amd as ssm
+    n = 1 << 28
+    x = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    _, ms_kernel, _ = time_steps(lambda: ssm.copy_f32(x, y), steps, warmup)
+    return 8.0 * n / (ms_kernel * 1e-3) / 1e9
+
+
+S6_BENCH = ["s6-fwd-b16-L1024-d256-N16-f32", "s6-fwd-b1-L65536-d1024-N16-bf16",
+            "s6-bidir-b4-L8192-d1536-N16-bf16"]
+
+
+def s6_algorithmic(w):
+    """Algorithmic HBM bytes and VALU lane-instructions per step.
+
+    Bytes: u and delta read once, y written once (fp32), B and C read once,
+    A and D read once. VALU per (b, t, d, n): delta*A, the exponential, dBu,
+    the state FMA and the output FMA (one exponential, four other
+    instructions); the bidirectional pass adds one state FMA and one output
+    FMA for the second direction (shared discretization).
+    """
+    es = 2 if w["dtype"] == "bf16" else 4
+    E = w["batch"] * w["L"] * w["d_inner"]
+    nbytes = E * (2 * es + 4) + 2 * w["batch"] * w["L"] * w["N"] * es + \
+        w["d_inner"] * (w["N"] + 1) * 4
+    other = 6 if w["direction"] == "bidir" else 4
+    return E, nbytes, E * w["N"], other
+
+
+def bench_s6(dev, name, steps, warmup, exp_cost):
+    import torch
+    import mamba_s6_selective_amd as ssm
+    from mamba_s6_selective_amd.workloads import S6_WORKLOADS, s6_workload_inputs
+    w = S6_WORKLOADS[name]
+    inp = s6_workload_inputs(name)
+    E, nbytes, tdn, other = s6_algorithmic(w)
+    # Rotate input sets so the working set exceeds the 256 MB Infinity Cache.
+    sets = max(1, min(8, int(1.0e9 // max(nbytes, 1)) + 1))
+    bufs = []
+    for _ in range(sets):
+        bufs.append([x.to(dev).clone() for x in (inp.u, inp.delta, inp.A, inp.B, inp.C, inp.D)]
+                    + [torch.empty(inp.u.shape, dtype=torch.float32, device=dev)])
+    k = [0]
+
+    def step():
+        t = bufs[k[0] % sets]
+        k[0] += 1
+        ssm.selective_scan_fwd(*t[:6], direction=w["direction"], out=t[6])
+
+    ms_step, ms_kernel, ms_min = time_steps(step, steps, warmup)
+    lane_cycles = tdn * (other + exp_cost)
+    alu_frac = lane_cycles / (ms_kernel * 1e-3) / (VALU_PEAK_T * 1e12)
+    gbs = nbytes / (ms_kernel * 1e-3) / 1e9
+    return {
+        "workload": name, "ms_per_step": round(ms_step, 4), "ms_kernel_avg": round(ms_kernel, 4),
+        "elements_per_s": E / (ms_step * 1e-3), "rotating_sets": sets,
+        "roofline": {"bound": "alu", "achieved": round(lane_cycles / (ms_kernel * 1e-3) / 1e12, 3),
+                     "peak": round(VALU_PEAK_T, 2), "unit": "T lane-cycles/s",
+                     "frac": round(alu_frac, 4), "exp_cost_lane_cycles": exp_cost,
+                     "traffic": None},
+        "hbm": {"achieved_GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": nbytes},
+    }
+
+
+def cpu_baseline(budget_s):
+    """The float64 C oracle on the same workload, single thread (the recurrence
+    is sequential), repeated for about `budget_s` seconds."""
+    import numpy as np
+    from mamba_s6_selective_amd.workloads import LINEAR_WORKLOADS, linear_workload_inputs
+    from oracle import native
+    n = LINEAR_WORKLOADS[LINEAR_WORKLOAD]["n"]
+    a, b = linear_workload_inputs(LINEAR_WORKLOAD)
+    a = a.numpy().astype(np.float64)
+    b = b.numpy().astype(np.float64)
+    native.load()
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while not times or (time.perf_counter() < t_end and len(times) < 50):
+        t0 = time.perf_counter()
+        native.linear_scan(a, b, 0.0)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": n / med, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole n=2^27 sequence, float64 C loop, {len(times)} passes "
+                      f"(median {med:.3f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-s6", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--exp-cost", type=float, default=2.0,
+                    help="lane-cycles one v_exp_f32 occupies relative to an FMA")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the scan runs on a single device and this "
+              "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mamba_s6_selective_amd as ssm
+    ssm.load_library()
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda:0")
+    if not sentinel_ok(dev):
+        raise SystemExit("sentinel copy kernel did not reproduce its input; sweep discarded")
+
+    copy_gbs = bench_copy(dev, 10, 3)
+    log(f"copy kernel: {copy_gbs:.0f} GB/s")
+    n, ms_step, ms_kernel, ms_min = bench_linear(dev, args.steps, args.warmup)
+    alg_bytes = LINEAR_BYTES_PER_ELEM * n
+    achieved = alg_bytes / (ms_kernel * 1e-3) / 1e9
+    log(f"linear scan: {ms_kernel * 1e3:.1f} us/launch (min {ms_min * 1e3:.1f}), "
+        f"{achieved:.0f} GB/s algorithmic")
+    traffic = load_traffic("linear_scan", "linear_scan.hip")
+    record = {
+        "metric": "scan elements/s + achieved HBM GB/s (% of MI355X peak), linear & S6 fwd",
+        "value": n / (ms_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded; pages' distributions)",
+        "config": {"workload": LINEAR_WORKLOAD, "n": n, "h0": 0.0,
+                   "a": "U(0.5,1)", "b": "N(0,1)", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "copy_kernel_GBs": round(copy_gbs, 1),
+    }
+    if not args.no_s6:
+        record["s6"] = [bench_s6(dev, name, max(5, args.steps // 2), 2, args.exp_cost)
+                        for name in S6_BENCH]
+        for r in record["s6"]:
+            log(f"{r['workload']}: {r['ms_kernel_avg'] * 1e3:.1f} us, "
+                f"alu frac {r['roofline']['frac']:.3f}, hbm frac {r['hbm']['frac_of_8TBs']:.3f}")
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

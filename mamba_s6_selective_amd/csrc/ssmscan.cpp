@@ -1,0 +1,278 @@
+// C-ABI entry points of libssmscan: argument checks, cached per-(device,
+// stream) workspaces, kernel dispatch and error reporting.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/ssmscan.h"
+#include "internal.h"
+#include "s6_internal.h"
+
+namespace ssm {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Workspace of the look-back linear scan for one (device, stream): tile
+// status words plus the ticket counter. Never reset between launches: each
+// launch uses a fresh epoch, and the ticket keeps counting up from where the
+// previous launch on this stream left it.
+struct LinearWorkspace {
+  TileStatus *status = nullptr;  // capacity entries
+  unsigned long long *ticket = nullptr;
+  int64_t capacity = 0;
+  unsigned long long ticket_next = 0;  // counter value when the next launch starts
+  uint32_t epoch = 0;                  // epoch of the last launch (0 = never)
+};
+
+struct S6Workspace {
+  void *buf = nullptr;
+  size_t bytes = 0;
+  unsigned long long *ticket = nullptr;
+  unsigned long long ticket_next = 0;
+  uint32_t epoch = 0;
+};
+
+using Key = std::pair<int, hipStream_t>;
+std::mutex g_mu;
+std::map<Key, LinearWorkspace> g_linear;
+std::map<Key, S6Workspace> g_s6;
+
+int current_device(int *dev) {
+  return hip_check(hipGetDevice(dev), "hipGetDevice");
+}
+}  // namespace
+
+int fail(int code, const std::string &msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_check(hipError_t e, const char *what) {
+  if (e == hipSuccess) return SSM_OK;
+  return fail(SSM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Returns a workspace holding at least `ntiles` status entries and reserves
+// `ntiles` tickets and a fresh epoch for one launch.
+static int linear_workspace(hipStream_t stream, int64_t ntiles, TileStatus **status,
+                            unsigned long long **ticket, unsigned long long *base,
+                            uint32_t *epoch) {
+  int dev = 0;
+  if (int rc = current_device(&dev)) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  LinearWorkspace &ws = g_linear[Key(dev, stream)];
+  if (ws.capacity < ntiles) {
+    if (ws.status) {
+      // The old buffers may still be read by launches queued on this stream.
+      if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
+      (void)hipFree(ws.status);
+      ws.status = nullptr;
+      ws.ticket = nullptr;
+      ws.capacity = 0;
+    }
+    int64_t cap = 1024;
+    while (cap < ntiles) cap *= 2;
+    const size_t bytes = size_t(cap) * sizeof(TileStatus) + 256;
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess)
+      return fail(SSM_ERR_ALLOC, "hipMalloc of the linear-scan workspace failed");
+    // Zero = epoch 0 everywhere (never written) and a ticket counter of 0.
+    if (int rc = hip_check(hipMemsetAsync(p, 0, bytes, stream), "hipMemsetAsync")) {
+      (void)hipFree(p);
+      return rc;
+    }
+    ws.status = static_cast<TileStatus *>(p);
+    ws.ticket = reinterpret_cast<unsigned long long *>(static_cast<char *>(p) +
+                                                       size_t(cap) * sizeof(TileStatus));
+    ws.capacity = cap;
+    ws.ticket_next = 0;
+  }
+  if (ws.epoch == 0xffffffffu) {
+    // Epochs are about to wrap: make every old word unambiguous again.
+    if (int rc = hip_check(hipMemsetAsync(ws.status, 0, size_t(ws.capacity) * sizeof(TileStatus),
+                                          stream), "hipMemsetAsync"))
+      return rc;
+    ws.epoch = 0;
+  }
+  ws.epoch += 1;
+  *status = ws.status;
+  *ticket = ws.ticket;
+  *base = ws.ticket_next;
+  *epoch = ws.epoch;
+  ws.ticket_next += (unsigned long long)ntiles;
+  return SSM_OK;
+}
+
+int s6_workspace(hipStream_t stream, size_t bytes, int64_t tickets, void **buf,
+                 unsigned long long **ticket, unsigned long long *base, uint32_t *epoch) {
+  int dev = 0;
+  if (int rc = current_device(&dev)) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  S6Workspace &ws = g_s6[Key(dev, stream)];
+  if (ws.bytes < bytes || ws.buf == nullptr) {
+    if (ws.buf) {
+      if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
+      (void)hipFree(ws.buf);
+      ws.buf = nullptr;
+      ws.bytes = 0;
+    }
+    size_t cap = 1 << 20;
+    while (cap < bytes) cap *= 2;
+    void *p = nullptr;
+    if (hipMalloc(&p, cap + 256) != hipSuccess)
+      return fail(SSM_ERR_ALLOC, "hipMalloc of the S6 workspace failed");
+    if (int rc = hip_check(hipMemsetAsync(p, 0, cap + 256, stream), "hipMemsetAsync")) {
+      (void)hipFree(p);
+      return rc;
+    }
+    ws.buf = p;
+    ws.bytes = cap;
+    ws.ticket = reinterpret_cast<unsigned long long *>(static_cast<char *>(p) + cap);
+    ws.ticket_next = 0;
+  }
+  if (ws.epoch == 0xffffffffu) {
+    if (int rc = hip_check(hipMemsetAsync(ws.buf, 0, ws.bytes, stream), "hipMemsetAsync"))
+      return rc;
+    ws.epoch = 0;
+  }
+  ws.epoch += 1;
+  *buf = ws.buf;
+  *ticket = ws.ticket;
+  *base = ws.ticket_next;
+  *epoch = ws.epoch;
+  ws.ticket_next += (unsigned long long)tickets;
+  return SSM_OK;
+}
+
+}  // namespace ssm
+
+using namespace ssm;
+
+extern "C" {
+
+int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t n,
+                    void *stream) {
+  g_last_error.clear();
+  if (n < 0) return fail(SSM_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return SSM_OK;
+  if (!a || !b || !h) return fail(SSM_ERR_INVALID_ARG, "null pointer with n > 0");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(h))
+    return fail(SSM_ERR_INVALID_ARG, "a, b and h must be 16-byte aligned");
+  const int64_t tile = linear_tile_elems();
+  const int64_t ntiles = (n + tile - 1) / tile;
+  if (ntiles > (int64_t(1) << 31) / 256)
+    return fail(SSM_ERR_UNSUPPORTED, "n too large for one launch");
+  TileStatus *status = nullptr;
+  unsigned long long *ticket = nullptr, base = 0;
+  uint32_t epoch = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int rc = linear_workspace(s, ntiles, &status, &ticket, &base, &epoch)) return rc;
+  return hip_check(launch_linear_scan(a, b, h0, h, n, ntiles, status, ticket, base, epoch, s),
+                   "linear_scan launch");
+}
+
+int ssm_copy_f32(const float *src, float *dst, int64_t n, void *stream) {
+  g_last_error.clear();
+  if (n < 0) return fail(SSM_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return SSM_OK;
+  if (!src || !dst) return fail(SSM_ERR_INVALID_ARG, "null pointer with n > 0");
+  if (!aligned16(src) || !aligned16(dst))
+    return fail(SSM_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  return hip_check(launch_copy_f32(src, dst, n, static_cast<hipStream_t>(stream)),
+                   "copy launch");
+}
+
+static int s6_check(const void *u, const void *delta, const float *A, const void *B,
+                    const void *C, const float *D, float *y, int batch, int L, int d_inner,
+                    int N, int direction, bool *noop) {
+  *noop = false;
+  if (batch < 0 || L < 0 || d_inner < 0 || N < 0)
+    return fail(SSM_ERR_INVALID_ARG, "sizes must be >= 0");
+  if (direction < SSM_DIR_FWD || direction > SSM_DIR_BIDIR)
+    return fail(SSM_ERR_INVALID_ARG, "direction must be 0 (fwd), 1 (rev) or 2 (bidir)");
+  if (N == 0) return fail(SSM_ERR_UNSUPPORTED, "N must be in 1..16");
+  if (N > kS6MaxN) return fail(SSM_ERR_UNSUPPORTED, "N must be in 1..16");
+  if (batch == 0 || L == 0 || d_inner == 0) {
+    *noop = true;
+    return SSM_OK;
+  }
+  if (!u || !delta || !A || !B || !C || !D || !y)
+    return fail(SSM_ERR_INVALID_ARG, "null pointer with non-zero sizes");
+  const void *ptrs[] = {u, delta, A, B, C, D, y};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (int64_t(batch) * L * d_inner > (int64_t(1) << 40))
+    return fail(SSM_ERR_UNSUPPORTED, "problem too large");
+  return SSM_OK;
+}
+
+int ssm_selective_scan_fwd(const float *u, const float *delta, const float *A,
+                           const float *B, const float *C, const float *D, float *y,
+                           int batch, int L, int d_inner, int N, int direction,
+                           void *stream) {
+  g_last_error.clear();
+  bool noop = false;
+  if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, &noop))
+    return rc;
+  if (noop) return SSM_OK;
+  S6Args args{u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, false};
+  return run_s6(args, static_cast<hipStream_t>(stream));
+}
+
+int ssm_selective_scan_fwd_bf16(const uint16_t *u, const uint16_t *delta, const float *A,
+                                const uint16_t *B, const uint16_t *C, const float *D,
+                                float *y, int batch, int L, int d_inner, int N,
+                                int direction, void *stream) {
+  g_last_error.clear();
+  bool noop = false;
+  if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, &noop))
+    return rc;
+  if (noop) return SSM_OK;
+  S6Args args{u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, true};
+  return run_s6(args, static_cast<hipStream_t>(stream));
+}
+
+const char *ssm_status_string(int code) {
+  switch (code) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_INVALID_ARG: return "invalid argument";
+    case SSM_ERR_UNSUPPORTED: return "unsupported argument";
+    case SSM_ERR_HIP: return "HIP runtime error";
+    case SSM_ERR_ALLOC: return "workspace allocation failed";
+    default: return "unknown status code";
+  }
+}
+
+const char *ssm_last_error(void) { return g_last_error.c_str(); }
+
+int ssm_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int rc = SSM_OK;
+  int saved = 0;
+  (void)hipGetDevice(&saved);
+  for (auto &kv : g_linear) {
+    if (!kv.second.status) continue;
+    (void)hipSetDevice(kv.first.first);
+    if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = SSM_ERR_HIP;
+    (void)hipFree(kv.second.status);
+  }
+  for (auto &kv : g_s6) {
+    if (!kv.second.buf) continue;
+    (void)hipSetDevice(kv.first.first);
+    if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = SSM_ERR_HIP;
+    (void)hipFree(kv.second.buf);
+  }
+  g_linear.clear();
+  g_s6.clear();
+  (void)hipSetDevice(saved);
+  return rc;
+}
+
+}  // extern "C"

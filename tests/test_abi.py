@@ -1,0 +1,93 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import mamba_s6_selective_amd as ssm
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "ssmscan.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("ssm_linear_scan", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_bf16"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssm.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in ssm.SIGNATURES, f"binding has no signature for {name}"
+
+
+def test_status_strings():
+    lib = ssm.load_library()
+    assert lib.ssm_status_string(0) == b"ok"
+    assert lib.ssm_status_string(-1) == b"invalid argument"
+    assert lib.ssm_status_string(12345) == b"unknown status code"
+
+
+# Argument errors are detected on the host before any HIP call, so they can be
+# exercised without a GPU. Pointers below are never dereferenced.
+FAKE = 0x1000          # 16-byte aligned, never dereferenced
+FAKE_MISALIGNED = 0x1004
+
+
+def test_linear_scan_argument_errors():
+    lib = ssm.load_library()
+    assert lib.ssm_linear_scan(None, None, 0.0, None, 0, None) == ssm.SSM_OK
+    assert lib.ssm_linear_scan(FAKE, FAKE, 0.0, FAKE, -1, None) == ssm.SSM_ERR_INVALID_ARG
+    assert b"n must be" in lib.ssm_last_error()
+    assert lib.ssm_linear_scan(None, FAKE, 0.0, FAKE, 5, None) == ssm.SSM_ERR_INVALID_ARG
+    assert lib.ssm_linear_scan(FAKE, FAKE_MISALIGNED, 0.0, FAKE, 5, None) == \
+        ssm.SSM_ERR_INVALID_ARG
+    assert b"aligned" in lib.ssm_last_error()
+
+
+@pytest.mark.parametrize("fn_name", ["ssm_selective_scan_fwd", "ssm_selective_scan_fwd_bf16"])
+def test_s6_argument_errors(fn_name):
+    lib = ssm.load_library()
+    fn = getattr(lib, fn_name)
+    P = [FAKE] * 7
+    # zero-sized problems are no-ops
+    assert fn(*P, 0, 10, 8, 16, 0, None) == ssm.SSM_OK
+    assert fn(*[None] * 7, 2, 0, 8, 16, 0, None) == ssm.SSM_OK
+    # negative sizes / bad direction
+    assert fn(*P, -1, 10, 8, 16, 0, None) == ssm.SSM_ERR_INVALID_ARG
+    assert fn(*P, 1, 10, 8, 16, 3, None) == ssm.SSM_ERR_INVALID_ARG
+    assert fn(*P, 1, 10, 8, 16, -1, None) == ssm.SSM_ERR_INVALID_ARG
+    # unsupported state sizes
+    assert fn(*P, 1, 10, 8, 17, 0, None) == ssm.SSM_ERR_UNSUPPORTED
+    assert fn(*P, 1, 10, 8, 0, 0, None) == ssm.SSM_ERR_UNSUPPORTED
+    # null / misaligned pointers with work to do
+    bad = list(P)
+    bad[3] = None
+    assert fn(*bad, 1, 10, 8, 16, 0, None) == ssm.SSM_ERR_INVALID_ARG
+    bad = list(P)
+    bad[6] = FAKE_MISALIGNED
+    assert fn(*bad, 1, 10, 8, 16, 0, None) == ssm.SSM_ERR_INVALID_ARG
+
+
+def test_copy_argument_errors():
+    lib = ssm.load_library()
+    assert lib.ssm_copy_f32(None, None, 0, None) == ssm.SSM_OK
+    assert lib.ssm_copy_f32(FAKE, None, 4, None) == ssm.SSM_ERR_INVALID_ARG
+    assert lib.ssm_copy_f32(FAKE, FAKE, -4, None) == ssm.SSM_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    a = torch.ones(8)
+    with pytest.raises(ValueError):
+        ssm.linear_scan(a, a)

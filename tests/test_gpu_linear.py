@@ -1,0 +1,130 @@
+"""GPU parity of the look-back linear scan against the float64 oracle.
+
+Bar: max |err| <= 1e-4 * (1 + |ref|) elementwise for fp32; bitwise identity
+across 100 repeated runs (the look-back always folds in the same order).
+"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import mamba_s6_selective_amd as ssm
+import oracle
+from gpu_util import assert_close, need_gpu, say
+from mamba_s6_selective_amd.workloads import linear_inputs, linear_workload_inputs
+from oracle import native
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+def run(a, b, h0=0.0):
+    dev = need_gpu()
+    h = ssm.linear_scan(a.to(dev), b.to(dev), h0)
+    torch.cuda.synchronize()
+    return h.cpu()
+
+
+def test_linear_n65536_workload():
+    say("linear-n65536 (a~U(0.9,1), b~N(0,1), h0=0)")
+    a, b = linear_workload_inputs("linear-n65536")
+    ref = oracle.linear_scan(a.numpy(), b.numpy(), 0.0)
+    assert_close(run(a, b).numpy(), ref, TOL, "linear-n65536")
+
+
+# sizes straddling lane chunks (4), rows (256), waves (1024), tiles (4096)
+EDGE_N = [1, 2, 3, 4, 5, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 4095, 4096,
+          4097, 8191, 8192, 12289, 65537, 100003, 262144 + 77]
+
+
+@pytest.mark.parametrize("n", EDGE_N)
+def test_linear_edge_sizes(n):
+    say(f"linear edge n={n}")
+    a, b = linear_inputs(n, seed=500 + n, a_lo=0.5, a_hi=1.0)
+    h0 = 0.75
+    ref = oracle.linear_scan(a.numpy(), b.numpy(), h0)
+    assert_close(run(a, b, h0).numpy(), ref, TOL, f"n={n}")
+
+
+def test_linear_zero_length_is_noop():
+    dev = need_gpu()
+    a = torch.empty(0, device=dev)
+    assert ssm.linear_scan(a, a, 1.0).numel() == 0
+
+
+def test_linear_signed_coefficients():
+    say("linear signed a ~ U(-1, 1), many tiles")
+    a, b = linear_inputs(300000, seed=77, a_lo=-1.0, a_hi=1.0)
+    ref = oracle.linear_scan(a.numpy(), b.numpy(), -2.0)
+    assert_close(run(a, b, -2.0).numpy(), ref, TOL, "signed")
+
+
+def test_linear_prefix_sum_exact():
+    """a == 1 with small integer b: every partial sum is an integer below 2^24,
+    so any association is exact and the result must equal the prefix sum."""
+    say("linear a=1 integer prefix sum, exact")
+    n = 1 << 20
+    g = torch.Generator().manual_seed(5)
+    b = torch.randint(-8, 9, (n,), generator=g).float()
+    a = torch.ones(n)
+    h = run(a, b, 3.0)
+    ref = 3.0 + np.cumsum(b.numpy().astype(np.float64))
+    assert np.array_equal(h.numpy().astype(np.float64), ref)
+
+
+def test_linear_reset_segments_exact():
+    """a in {0, 1}, integer b: segmented prefix sums, exact."""
+    say("linear a in {0,1} segmented, exact")
+    n = 200000
+    g = torch.Generator().manual_seed(6)
+    a = (torch.rand(n, generator=g) < 0.999).float()
+    b = torch.randint(-8, 9, (n,), generator=g).float()
+    ref = native.linear_scan(a.numpy(), b.numpy(), 1.0)
+    assert np.array_equal(run(a, b, 1.0).numpy().astype(np.float64), ref)
+
+
+def test_linear_nan_propagates_without_hang():
+    say("linear NaN propagation")
+    n = 50000
+    a, b = linear_inputs(n, seed=9, a_lo=0.5, a_hi=1.0)
+    b[20000] = float("nan")
+    ref = oracle.linear_scan(a.numpy(), b.numpy(), 0.0)
+    assert_close(run(a, b).numpy(), ref, TOL, "nan")
+
+
+def test_linear_full_size_workload():
+    say("linear-n134217728 full size vs C oracle")
+    dev = need_gpu()
+    a, b = linear_workload_inputs("linear-n134217728")
+    h = ssm.linear_scan(a.to(dev), b.to(dev), 0.0)
+    torch.cuda.synchronize()
+    ref = native.linear_scan(a.numpy(), b.numpy(), 0.0)
+    assert_close(h.cpu().numpy(), ref, TOL, "linear-n134217728")
+
+
+@pytest.mark.parametrize("n", [1 << 27, (1 << 20) + 3])
+def test_linear_bitwise_determinism_100_runs(n):
+    say(f"linear determinism 100 runs n={n}")
+    dev = need_gpu()
+    a, b = linear_inputs(n, seed=31, a_lo=0.5, a_hi=1.0)
+    a, b = a.to(dev), b.to(dev)
+    first = ssm.linear_scan(a, b, 0.5)
+    out = torch.empty_like(first)
+    mismatches = 0
+    for _ in range(99):
+        ssm.linear_scan(a, b, 0.5, out=out)
+        if not torch.equal(out.view(torch.int32), first.view(torch.int32)):
+            mismatches += 1
+    torch.cuda.synchronize()
+    digest = hashlib.sha256(first.cpu().numpy().tobytes()).hexdigest()[:16]
+    say(f"  sha256 {digest}, mismatching runs: {mismatches}")
+    assert mismatches == 0
+
+
+def test_copy_sentinel():
+    dev = need_gpu()
+    x = torch.randn(1000003, device=dev)
+    y = torch.empty_like(x)
+    ssm.copy_f32(x, y)
+    assert torch.equal(x, y)
