@@ -16,28 +16,39 @@ int hip_check(hipError_t e, const char *what);
 
 // ---- linear recurrence -----------------------------------------------------
 
-// Per-tile status, written with single 64-bit relaxed atomic stores at agent
-// scope. Each word carries the launch's 32-bit epoch in its high half and a
-// 32-bit float payload in its low half, so a word is either "not yet written
-// in this launch" (epoch differs) or complete; no fence pairs are needed and a
-// NaN payload cannot be mistaken for a flag.
-struct TileStatus {
-  uint64_t agg_a;  // (epoch << 32) | bits(tile aggregate multiplier)
-  uint64_t agg_b;  // (epoch << 32) | bits(tile aggregate offset)
-  uint64_t inc;    // (epoch << 32) | bits(h at the end of the tile)
-  uint64_t pad;
+// One published affine aggregate: two 64-bit words written with relaxed
+// agent-scope atomic stores. Each word carries the launch's 32-bit epoch in its
+// high half and an fp32 payload in its low half, so a word is either "not yet
+// written in this launch" (epoch differs) or complete; no fence pairs are
+// needed and a NaN payload cannot be mistaken for a flag.
+struct AggWord {
+  uint64_t a;  // (epoch << 32) | bits(multiplier)
+  uint64_t b;  // (epoch << 32) | bits(offset)
 };
+
+// Status of one launch: aggregates of tiles (level 0), of superblocks of 64
+// tiles (level 1) and of blocks of 64 superblocks (level 2).
+struct LinearStatus {
+  AggWord *lvl0;
+  AggWord *lvl1;
+  AggWord *lvl2;
+};
+
+// Largest tile count one launch supports (three levels of 64).
+constexpr int64_t kLinearMaxTiles = int64_t(64) * 64 * 64;
 
 // Elements per tile of the look-back scan.
 int64_t linear_tile_elems();
 
-// Enqueues the single-pass scan. status must hold ntiles entries whose
-// epochs differ from `epoch`; *ticket must equal ticket_base at launch start.
+// Enqueues the single-pass scan as a cooperative launch of
+// min(ntiles, resident_wgs) persistent workgroups. The status levels must hold
+// ntiles, ceil(ntiles/64) and ceil(ntiles/4096) entries whose epochs differ
+// from `epoch`.
 hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h,
-                              int64_t n, int64_t ntiles, TileStatus *status,
-                              unsigned long long *ticket,
-                              unsigned long long ticket_base, uint32_t epoch,
-                              hipStream_t stream);
+                              int64_t n, int64_t ntiles, LinearStatus status, uint32_t epoch,
+                              int resident_wgs, hipStream_t stream);
+// Workgroups of the scan kernel that fit on one CU at once (0 on error).
+int linear_wgs_per_cu();
 
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n,
                            hipStream_t stream);

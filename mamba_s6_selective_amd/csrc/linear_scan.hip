@@ -1,4 +1,4 @@
-// Single-pass decoupled look-back scan of the affine recurrence
+// Single-pass look-back scan of the affine recurrence
 //   h[t] = a[t] * h[t-1] + b[t],  h[-1] = h0
 // for gfx950 (CDNA4, wave64).
 //
@@ -7,27 +7,39 @@
 // earlier map on the left ("Selective-scan CUDA kernels", the paragraph on the
 // recurrence). The page's fastest design is a single-pass decoupled look-back
 // with several items per thread scanned in registers and a warp-wide
-// inspection of predecessors; this kernel keeps that structure and re-plans it
-// for wave64, DPP and the multi-XCD memory system:
+// inspection of predecessors. This kernel keeps the single pass, the
+// register-resident items and the wave-wide inspection, and re-plans the
+// cross-tile protocol for a part whose workgroups sit on 8 XCDs with private
+// L2s, where a published word takes on the order of a microsecond to become
+// visible to another XCD:
 //
-//  * tile = 4 waves x 4 rows x 64 lanes x float4 = 4096 elements. Each row is
+//  * tile = 4 waves x 8 rows x 64 lanes x float4 = 8192 elements. Each row is
 //    read and written with one fully coalesced 1 KiB global_load/store_dwordx4
-//    per wave, so no LDS transpose is needed.
-//  * per lane: 4-element chunk aggregates in registers; per row: a wave64
-//    inclusive scan of chunk aggregates with DPP row_shr / row_bcast steps;
-//    per wave and per tile: short serial folds of 4 values.
-//  * tile order comes from an atomic ticket, so every predecessor of a running
-//    tile is itself running and will publish: forward progress holds.
-//  * the status of a tile is three 64-bit words, each (epoch | fp32 payload),
-//    written and read with relaxed agent-scope atomics. The payload is its own
-//    flag, so there are no release/acquire fences (which would write back or
-//    invalidate a whole L2 on this multi-XCD part) and no per-launch reset.
-//  * look-back: wave 0 reads 64 predecessors per step (lane i -> tile k-1-i),
-//    ballots for the nearest one whose inclusive value is published, and then
-//    folds the aggregates in between strictly left to right, one lane at a
-//    time. Every tile's inclusive value is therefore the same left fold
-//    inc(k) = fma(G_k.a, inc(k-1), G_k.b) whichever predecessor was found,
-//    which makes the output bitwise identical from run to run.
+//    per wave (no LDS transpose). Per lane: 4-element chunk aggregates in
+//    registers; per row: a wave64 inclusive scan of chunk aggregates with DPP
+//    row_shr / row_bcast steps; per wave and per tile: short serial folds.
+//  * no inclusive-prefix chain. A classic look-back publishes each tile's
+//    inclusive prefix, and the published frontier then advances by at most
+//    one inspection window per visibility round trip. Here every tile only
+//    publishes aggregates, at three levels: its own (level 0), that of its
+//    superblock of 64 tiles (level 1, published by the superblock's last
+//    tile), and that of its block of 64 superblocks (level 2, published by
+//    the block's last tile). A tile's incoming value is h0 pushed through the
+//    composition of at most 63 level-2, 63 level-1 and 63 level-0 aggregates,
+//    each window composed by one fixed-shape wave64 DPP scan. Every wait is on
+//    aggregates that depend only on loads of earlier tiles, so a tile waits a
+//    bounded number of round trips, whatever the size of the input.
+//  * deterministic: the window contents and the shape of every composition are
+//    fixed by the tile index alone, so the output is bitwise identical from
+//    run to run.
+//  * status words are 64-bit (epoch | fp32 payload), written and read with
+//    relaxed agent-scope atomics. The payload is its own flag, so there are no
+//    release/acquire fences (which would write back or invalidate a whole L2)
+//    and no per-launch reset.
+//  * the kernel is persistent and launched cooperatively: every workgroup is
+//    resident and walks its tiles in increasing order, and a tile only waits
+//    for words published by lower tiles before they wait on anything, so the
+//    lowest unfinished tile can always finish.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,11 +49,12 @@ namespace ssm {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRows = 4;
+constexpr int kRows = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowElems = 256;                    // 64 lanes x float4
-constexpr int kWaveElems = kRowElems * kRows;     // 1024
-constexpr int kTileElems = kWaveElems * kWaves;   // 4096
+constexpr int kWaveElems = kRowElems * kRows;     // 2048
+constexpr int kTileElems = kWaveElems * kWaves;   // 8192
+constexpr int kFan = 64;                          // entries per look-back window
 
 // DPP controls (GFX9 encoding).
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
@@ -90,72 +103,101 @@ __device__ __forceinline__ float payload(uint64_t w) {
   return __uint_as_float(uint32_t(w));
 }
 
-// h value entering tile `tile` (> 0): nearest published inclusive value of a
-// predecessor, then the aggregates after it folded one by one, oldest first.
-// Called by all 64 lanes of one wave; returns the same value in every lane.
-__device__ float look_back(const TileStatus *st, int64_t tile, uint32_t epoch, int lane) {
-  int64_t base = tile - 1;  // lane 0 inspects `base`, lane i inspects base - i
-  int skipped = 0;          // whole windows of aggregates passed over so far
-  for (;;) {
-    const int64_t idx = base - lane;
-    const bool valid = idx >= 0;
-    uint64_t wi = 0, wa = 0, wb = 0;
-    if (valid) {
-      wi = ld_status(&st[idx].inc);
-      wa = ld_status(&st[idx].agg_a);
-      wb = ld_status(&st[idx].agg_b);
-    }
-    const bool is_inc = valid && uint32_t(wi >> 32) == epoch;
-    const bool is_agg = valid && uint32_t(wa >> 32) == epoch && uint32_t(wb >> 32) == epoch;
-    const uint64_t inc_mask = __ballot(is_inc);
-    const uint64_t agg_mask = __ballot(is_agg);
-    if (inc_mask != 0) {
-      const int p = __builtin_ctzll(inc_mask);
-      const uint64_t nearer = (p == 0) ? 0ull : ((1ull << p) - 1ull);
-      if ((agg_mask & nearer) == nearer) {
-        const float fa = payload(wa), fb = payload(wb);
-        float h = lane_f(payload(wi), p);
-        for (int l = p - 1; l >= 0; --l) h = __builtin_fmaf(lane_f(fa, l), h, lane_f(fb, l));
-        // Windows passed over earlier are newer than this one: fold them in,
-        // oldest (largest lane, farthest window) first. They are all complete.
-        for (int w = 1; w <= skipped; ++w) {
-          const int64_t j = base + 64 * w - lane;
-          const float ga = payload(ld_status(&st[j].agg_a));
-          const float gb = payload(ld_status(&st[j].agg_b));
-          for (int l = 63; l >= 0; --l) h = __builtin_fmaf(lane_f(ga, l), h, lane_f(gb, l));
-        }
-        return h;
-      }
-    } else if ((agg_mask | ~__ballot(valid)) == ~0ull) {
-      base -= 64;  // a full window of aggregates and no inclusive: look further back
-      ++skipped;
-      continue;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
+__device__ __forceinline__ bool word_ready(uint64_t w, uint32_t epoch) {
+  return uint32_t(w >> 32) == epoch;
 }
 
-__global__ __launch_bounds__(kThreads) void linear_scan_kernel(
-    const float *__restrict__ a, const float *__restrict__ b, float h0,
-    float *__restrict__ h, int64_t n, int64_t ntiles, TileStatus *__restrict__ st,
-    unsigned long long *__restrict__ ticket, unsigned long long ticket_base,
-    uint32_t epoch) {
-  __shared__ int64_t s_tile;
-  __shared__ float s_wave_a[kWaves], s_wave_b[kWaves], s_carry[kWaves];
+// Composition, in lane order, of the pairs held by lanes [0, count) of the
+// wave (later lanes contribute the identity). Fixed DPP tree: the result
+// depends only on the values and `count`. Returned in every lane.
+__device__ __forceinline__ void window_total(float a, float b, int count, int lane, float &ta,
+                                             float &tb) {
+  if (lane >= count) {
+    a = 1.0f;
+    b = 0.0f;
+  }
+  wave_scan(a, b);
+  ta = lane_f(a, 63);
+  tb = lane_f(b, 63);
+}
 
+// Incoming value of `tile`, composed from published aggregates (see the file
+// comment). The last tile of a superblock also publishes the superblock's
+// aggregate, and the last tile of a block the block's aggregate, as soon as
+// their inputs are visible. Called by all 64 lanes of one wave.
+__device__ float look_back(const LinearStatus &st, int64_t tile, float ga, float gb, float h0,
+                           uint32_t epoch, int lane) {
+  const int64_t sb = tile / kFan;             // superblock of this tile
+  const int64_t blk = sb / kFan;              // block of this tile
+  const int n0 = int(tile - sb * kFan);       // level-0 entries before the tile in its superblock
+  const int n1 = int(sb - blk * kFan);        // level-1 entries before its superblock in its block
+  const int n2 = int(blk);                    // level-2 entries before its block
+  const bool last_in_sb = n0 == kFan - 1;
+  const bool last_in_blk = last_in_sb && n1 == kFan - 1;
+  const bool need0 = lane < n0, need1 = lane < n1, need2 = lane < n2;
+  const int64_t i0 = sb * kFan + lane, i1 = blk * kFan + lane, i2 = lane;
+  uint64_t w0a = 0, w0b = 0, w1a = 0, w1b = 0, w2a = 0, w2b = 0;
+  bool r0 = !need0, r1 = !need1, r2 = !need2;
+  bool pub1 = !last_in_sb, pub2 = !last_in_blk;
+  float sa = 1.0f, sbv = 0.0f;  // this superblock's aggregate, when published here
+  for (;;) {
+    if (!r0) {
+      w0a = ld_status(&st.lvl0[i0].a);
+      w0b = ld_status(&st.lvl0[i0].b);
+      r0 = word_ready(w0a, epoch) && word_ready(w0b, epoch);
+    }
+    if (!r1) {
+      w1a = ld_status(&st.lvl1[i1].a);
+      w1b = ld_status(&st.lvl1[i1].b);
+      r1 = word_ready(w1a, epoch) && word_ready(w1b, epoch);
+    }
+    if (!r2) {
+      w2a = ld_status(&st.lvl2[i2].a);
+      w2b = ld_status(&st.lvl2[i2].b);
+      r2 = word_ready(w2a, epoch) && word_ready(w2b, epoch);
+    }
+    const bool all0 = __ballot(!r0) == 0, all1 = __ballot(!r1) == 0, all2 = __ballot(!r2) == 0;
+    if (!pub1 && all0) {
+      float pa, pb;
+      window_total(payload(w0a), payload(w0b), n0, lane, pa, pb);
+      sbv = __builtin_fmaf(ga, pb, gb);  // (P0 (+) own aggregate)
+      sa = pa * ga;
+      if (lane == 0) {
+        st_status(&st.lvl1[sb].a, epoch, sa);
+        st_status(&st.lvl1[sb].b, epoch, sbv);
+      }
+      pub1 = true;
+    }
+    if (!pub2 && pub1 && all1) {
+      float pa, pb;
+      window_total(payload(w1a), payload(w1b), n1, lane, pa, pb);
+      if (lane == 0) {
+        st_status(&st.lvl2[blk].a, epoch, pa * sa);
+        st_status(&st.lvl2[blk].b, epoch, __builtin_fmaf(sa, pb, sbv));
+      }
+      pub2 = true;
+    }
+    if (all0 && all1 && all2 && pub1 && pub2) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  float p0a, p0b, p1a, p1b, p2a, p2b;
+  window_total(payload(w0a), payload(w0b), n0, lane, p0a, p0b);
+  window_total(payload(w1a), payload(w1b), n1, lane, p1a, p1b);
+  window_total(payload(w2a), payload(w2b), n2, lane, p2a, p2b);
+  const float h2 = __builtin_fmaf(p2a, h0, p2b);
+  const float h1 = __builtin_fmaf(p1a, h2, p1b);
+  return __builtin_fmaf(p0a, h1, p0b);
+}
+
+// One tile: load, scan in registers, publish, look back, apply, store.
+__device__ __forceinline__ void scan_tile(const float *__restrict__ a,
+                                          const float *__restrict__ b, float h0,
+                                          float *__restrict__ h, int64_t n, int64_t tile,
+                                          const LinearStatus &st, uint32_t epoch,
+                                          float *s_wave_a, float *s_wave_b, float *s_carry) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-
-  if (tid == 0) {
-    const unsigned long long t =
-        __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_tile = int64_t(t - ticket_base);
-  }
-  __syncthreads();
-  const int64_t tile = s_tile;
-  if (tile < 0 || tile >= ntiles) return;  // stale ticket base: never touch memory
-
   const int64_t wave_start = tile * kTileElems + int64_t(wave) * kWaveElems;
   const bool full = (tile + 1) * kTileElems <= n;
 
@@ -217,18 +259,12 @@ __global__ __launch_bounds__(kThreads) void linear_scan_kernel(
       gb = __builtin_fmaf(s_wave_a[w], gb, s_wave_b[w]);
       ga *= s_wave_a[w];
     }
-    float h_in;
-    if (tile == 0) {
-      h_in = h0;
-    } else {
-      if (lane == 0) {
-        st_status(&st[tile].agg_a, epoch, ga);
-        st_status(&st[tile].agg_b, epoch, gb);
-      }
-      h_in = look_back(st, tile, epoch, lane);
-    }
     if (lane == 0) {
-      st_status(&st[tile].inc, epoch, __builtin_fmaf(ga, h_in, gb));
+      st_status(&st.lvl0[tile].a, epoch, ga);
+      st_status(&st.lvl0[tile].b, epoch, gb);
+    }
+    const float h_in = look_back(st, tile, ga, gb, h0, epoch, lane);
+    if (lane == 0) {
       float c = h_in;
       for (int w = 0; w < kWaves; ++w) {
         s_carry[w] = c;
@@ -263,6 +299,21 @@ __global__ __launch_bounds__(kThreads) void linear_scan_kernel(
   }
 }
 
+// Persistent kernel: launched cooperatively, so all gridDim.x workgroups are
+// resident at once. Workgroup w scans tiles w, w + G, w + 2G, ... in order.
+// A tile only waits for lower-numbered tiles, each of which belongs to a
+// resident workgroup that reaches it after finishing its own lower tiles;
+// the lowest unfinished tile can therefore always finish (no ticket needed).
+__global__ __launch_bounds__(kThreads) void linear_scan_kernel(
+    const float *__restrict__ a, const float *__restrict__ b, float h0,
+    float *__restrict__ h, int64_t n, int64_t ntiles, LinearStatus st, uint32_t epoch) {
+  __shared__ float s_wave_a[kWaves], s_wave_b[kWaves], s_carry[kWaves];
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    scan_tile(a, b, h0, h, n, tile, st, epoch, s_wave_a, s_wave_b, s_carry);
+    __syncthreads();  // s_carry is rewritten by the next tile
+  }
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(const float *__restrict__ src,
                                                    float *__restrict__ dst, int64_t n) {
   const int64_t nvec = n / 4;
@@ -278,13 +329,22 @@ __global__ __launch_bounds__(256) void copy_kernel(const float *__restrict__ src
 int64_t linear_tile_elems() { return kTileElems; }
 
 hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h,
-                              int64_t n, int64_t ntiles, TileStatus *status,
-                              unsigned long long *ticket,
-                              unsigned long long ticket_base, uint32_t epoch,
-                              hipStream_t stream) {
-  hipLaunchKernelGGL(linear_scan_kernel, dim3(unsigned(ntiles)), dim3(kThreads), 0, stream,
-                     a, b, h0, h, n, ntiles, status, ticket, ticket_base, epoch);
-  return hipGetLastError();
+                              int64_t n, int64_t ntiles, LinearStatus status, uint32_t epoch,
+                              int resident_wgs, hipStream_t stream) {
+  const unsigned grid = unsigned(ntiles < resident_wgs ? ntiles : resident_wgs);
+  void *args[] = {(void *)&a, (void *)&b, (void *)&h0, (void *)&h,
+                  (void *)&n, (void *)&ntiles, (void *)&status, (void *)&epoch};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(linear_scan_kernel),
+                                    dim3(grid), dim3(kThreads), args, 0, stream);
+}
+
+int linear_wgs_per_cu() {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void *>(linear_scan_kernel), kThreads, 0) !=
+      hipSuccess)
+    return 0;
+  return per_cu;
 }
 
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t stream) {

@@ -47,6 +47,42 @@ __device__ __forceinline__ float ldv(const uint16_t *p) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Element at a wave-uniform base plus a per-lane 32-bit byte offset: lets the
+// compiler use the scalar-base + 32-bit-offset form of global loads/stores
+// instead of per-lane 64-bit address arithmetic on the VALU.
+template <typename T>
+__device__ __forceinline__ T &at(T *base, uint32_t byte_off) {
+  return *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ const T &at(const T *base, uint32_t byte_off) {
+  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+// Loads the N-long row p[0..NT) (wave-uniform address) as fp32. bf16 rows of
+// even length are read as 32-bit words so that the loads stay scalar and the
+// widening to fp32 (a shift or a mask) runs on the scalar unit.
+template <int NT>
+__device__ __forceinline__ void load_row(const float *__restrict__ p, float (&out)[NT]) {
+#pragma unroll
+  for (int n = 0; n < NT; ++n) out[n] = p[n];
+}
+template <int NT>
+__device__ __forceinline__ void load_row(const uint16_t *__restrict__ p, float (&out)[NT]) {
+  if constexpr (NT % 2 == 0) {
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i) {
+      const uint32_t v = w[i];
+      out[2 * i] = __uint_as_float(v << 16);
+      out[2 * i + 1] = __uint_as_float(v & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) out[n] = ldv(p + n);
+  }
+}
+
 struct Geometry {
   int batch, L, d_inner, groups, nchunks, chunk;
 };
@@ -66,37 +102,71 @@ __device__ __forceinline__ size_t agg_index(const Geometry &g, int NT, int b, in
   return ((size_t(b) * g.nchunks + c) * NT + n) * g.d_inner + d;
 }
 
+constexpr int kPrefetch = 8;  // steps of u/delta (and y) kept in flight per lane
+
 // One sweep of the chunk-local recurrence from a zero state. Writes (or, when
-// `accumulate`, adds) y for every step of the chunk and leaves the final state
-// in h and the sum of delta in S.
-template <typename T, int NT, bool Reverse>
+// Accumulate, adds) y for every step of the chunk and leaves the final state
+// in h and the sum of delta in S. Per-lane words for the next kPrefetch steps
+// are loaded ahead in a register ring; B[t] and C[t] are wave-uniform scalar
+// loads.
+template <typename T, int NT, bool Reverse, bool Accumulate>
 __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__restrict__ delta,
                                             const T *__restrict__ B, const T *__restrict__ C,
                                             float *__restrict__ y, const float (&Ap)[NT],
                                             float Dd, const Geometry &g, int b, int d, int t0,
-                                            int t1, bool accumulate, float (&h)[NT], float &S) {
+                                            int t1, float (&h)[NT], float &S) {
 #pragma unroll
   for (int n = 0; n < NT; ++n) h[n] = 0.0f;
   S = 0.0f;
   const size_t row0 = size_t(b) * g.L;
-  for (int i = 0; i < t1 - t0; ++i) {
+  const int len = t1 - t0;
+  // Wave-uniform offset of step i's (b, t, 0) element; the lane adds d.
+  auto row = [&](int i) {
     const int t = Reverse ? (t1 - 1 - i) : (t0 + i);
-    const size_t e = (row0 + t) * g.d_inner + d;
-    const float dt = ldv(delta + e);
-    const float x = ldv(u + e);
-    const T *Bt = B + (row0 + t) * NT;
-    const T *Ct = C + (row0 + t) * NT;
-    const float du = dt * x;
-    float acc = 0.0f;
+    return (row0 + t) * size_t(g.d_inner);
+  };
+  const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));  // input byte offset of the lane
+  const uint32_t yo = uint32_t(d) * 4u;                    // output byte offset of the lane
+  float rd[kPrefetch], rx[kPrefetch], ry[kPrefetch];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const float dA = exp2_hw(dt * Ap[n]);
-      h[n] = __builtin_fmaf(dA, h[n], du * ldv(Bt + n));
-      acc = __builtin_fmaf(ldv(Ct + n), h[n], acc);
+  for (int j = 0; j < kPrefetch; ++j) {
+    if (j < len) {
+      const size_t r = row(j);
+      rd[j] = ldv(&at(delta + r, io));
+      rx[j] = ldv(&at(u + r, io));
+      if (Accumulate) ry[j] = at(y + r, yo);
     }
-    const float out = __builtin_fmaf(Dd, x, acc);
-    y[e] = accumulate ? y[e] + out : out;
-    S += dt;
+  }
+  for (int i0 = 0; i0 < len; i0 += kPrefetch) {
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+      const int i = i0 + j;
+      if (i < len) {
+        const float dt = rd[j], x = rx[j];
+        const float yprev = Accumulate ? ry[j] : 0.0f;
+        if (i + kPrefetch < len) {
+          const size_t rn = row(i + kPrefetch);
+          rd[j] = ldv(&at(delta + rn, io));
+          rx[j] = ldv(&at(u + rn, io));
+          if (Accumulate) ry[j] = at(y + rn, yo);
+        }
+        const int t = Reverse ? (t1 - 1 - i) : (t0 + i);
+        float Bt[NT], Ct[NT];
+        load_row<NT>(B + (row0 + t) * NT, Bt);
+        load_row<NT>(C + (row0 + t) * NT, Ct);
+        const float du = dt * x;
+        float acc = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const float dA = exp2_hw(dt * Ap[n]);
+          h[n] = __builtin_fmaf(dA, h[n], du * Bt[n]);
+          acc = __builtin_fmaf(Ct[n], h[n], acc);
+        }
+        const float out = __builtin_fmaf(Dd, x, acc);
+        at(y + row(i), yo) = Accumulate ? yprev + out : out;
+        S += dt;
+      }
+    }
   }
 }
 
@@ -119,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
   float S = 0.0f;
   const bool multi = g.nchunks > 1;
   if (direction != SSM_DIR_REV) {
-    chunk_sweep<T, NT, false>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1, false, h, S);
+    chunk_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1, h, S);
     if (multi) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
@@ -129,8 +199,10 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
     }
   }
   if (direction != SSM_DIR_FWD) {
-    chunk_sweep<T, NT, true>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1,
-                             direction == SSM_DIR_BIDIR, h, S);
+    if (direction == SSM_DIR_BIDIR)
+      chunk_sweep<T, NT, true, true>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1, h, S);
+    else
+      chunk_sweep<T, NT, true, false>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1, h, S);
     if (multi) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
@@ -143,6 +215,10 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
 
 // Per (b, n, d): incoming state of every chunk, by a sequential left fold of
 // the chunk aggregates (forward: chunk 0 upwards; reverse: last chunk down).
+// Aggregates are loaded kGroup at a time before being folded, so the loads of
+// a group are in flight together rather than one dependent load per chunk.
+constexpr int kGroup = 16;
+
 __global__ __launch_bounds__(kThreads) void s6_carry_kernel(
     const float *__restrict__ agg_a, const float *__restrict__ agg_f,
     const float *__restrict__ agg_r, float *__restrict__ carry_f, float *__restrict__ carry_r,
@@ -154,20 +230,31 @@ __global__ __launch_bounds__(kThreads) void s6_carry_kernel(
   const int rem = int(idx % per_b);  // n * d_inner + d
   const size_t stride = size_t(NT) * g.d_inner;
   const size_t base = size_t(b) * g.nchunks * stride + rem;
-  if (direction != SSM_DIR_REV) {
+  for (int dir = 0; dir < 2; ++dir) {
+    if (dir == 0 && direction == SSM_DIR_REV) continue;
+    if (dir == 1 && direction == SSM_DIR_FWD) continue;
+    const float *aggb = dir == 0 ? agg_f : agg_r;
+    float *carry = dir == 0 ? carry_f : carry_r;
     float c = 0.0f;
-    for (int k = 0; k < g.nchunks; ++k) {
-      const size_t i = base + size_t(k) * stride;
-      carry_f[i] = c;
-      c = __builtin_fmaf(agg_a[i], c, agg_f[i]);
-    }
-  }
-  if (direction != SSM_DIR_FWD) {
-    float c = 0.0f;
-    for (int k = g.nchunks - 1; k >= 0; --k) {
-      const size_t i = base + size_t(k) * stride;
-      carry_r[i] = c;
-      c = __builtin_fmaf(agg_a[i], c, agg_r[i]);
+    for (int k0 = 0; k0 < g.nchunks; k0 += kGroup) {
+      float ga[kGroup], gb[kGroup];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const int k = dir == 0 ? k0 + j : g.nchunks - 1 - (k0 + j);
+        if (k0 + j < g.nchunks) {
+          const size_t i = base + size_t(k) * stride;
+          ga[j] = agg_a[i];
+          gb[j] = aggb[i];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const int k = dir == 0 ? k0 + j : g.nchunks - 1 - (k0 + j);
+        if (k0 + j < g.nchunks) {
+          carry[base + size_t(k) * stride] = c;
+          c = __builtin_fmaf(ga[j], c, gb[j]);
+        }
+      }
     }
   }
 }
@@ -178,17 +265,43 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
                                           const float (&cin)[NT], const Geometry &g, int b,
                                           int d, int t0, int t1) {
   const size_t row0 = size_t(b) * g.L;
-  float S = 0.0f;
-  for (int i = 0; i < t1 - t0; ++i) {
+  const int len = t1 - t0;
+  auto row = [&](int i) {
     const int t = Reverse ? (t1 - 1 - i) : (t0 + i);
-    const size_t e = (row0 + t) * g.d_inner + d;
-    S += ldv(delta + e);
-    const T *Ct = C + (row0 + t) * NT;
-    float acc = 0.0f;
+    return (row0 + t) * size_t(g.d_inner);
+  };
+  const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));
+  const uint32_t yo = uint32_t(d) * 4u;
+  float rd[kPrefetch], ry[kPrefetch];
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      acc = __builtin_fmaf(ldv(Ct + n), cin[n] * exp2_hw(Ap[n] * S), acc);
-    y[e] += acc;
+  for (int j = 0; j < kPrefetch; ++j) {
+    if (j < len) {
+      rd[j] = ldv(&at(delta + row(j), io));
+      ry[j] = at(y + row(j), yo);
+    }
+  }
+  float S = 0.0f;
+  for (int i0 = 0; i0 < len; i0 += kPrefetch) {
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+      const int i = i0 + j;
+      if (i < len) {
+        S += rd[j];
+        const float yprev = ry[j];
+        if (i + kPrefetch < len) {
+          rd[j] = ldv(&at(delta + row(i + kPrefetch), io));
+          ry[j] = at(y + row(i + kPrefetch), yo);
+        }
+        const int t = Reverse ? (t1 - 1 - i) : (t0 + i);
+        float Ct[NT];
+        load_row<NT>(C + (row0 + t) * NT, Ct);
+        float acc = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          acc = __builtin_fmaf(Ct[n], cin[n] * exp2_hw(Ap[n] * S), acc);
+        at(y + row(i), yo) = yprev + acc;
+      }
+    }
   }
 }
 

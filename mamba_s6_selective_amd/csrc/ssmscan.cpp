@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <stdlib.h>
+
 #include <map>
 #include <mutex>
 #include <string>
@@ -19,16 +21,12 @@ thread_local std::string g_last_error;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Workspace of the look-back linear scan for one (device, stream): tile
-// status words plus the ticket counter. Never reset between launches: each
-// launch uses a fresh epoch, and the ticket keeps counting up from where the
-// previous launch on this stream left it.
+// Workspace of the look-back linear scan for one (device, stream): the tile
+// status words. Never reset between launches: each launch uses a fresh epoch.
 struct LinearWorkspace {
-  TileStatus *status = nullptr;  // capacity entries
-  unsigned long long *ticket = nullptr;
-  int64_t capacity = 0;
-  unsigned long long ticket_next = 0;  // counter value when the next launch starts
-  uint32_t epoch = 0;                  // epoch of the last launch (0 = never)
+  AggWord *words = nullptr;  // capacity + capacity/64 + capacity/4096 entries
+  int64_t capacity = 0;      // tiles
+  uint32_t epoch = 0;        // epoch of the last launch (0 = never)
 };
 
 struct S6Workspace {
@@ -43,6 +41,7 @@ using Key = std::pair<int, hipStream_t>;
 std::mutex g_mu;
 std::map<Key, LinearWorkspace> g_linear;
 std::map<Key, S6Workspace> g_s6;
+std::map<int, int> g_linear_grid;  // device -> resident workgroups of the scan kernel
 
 int current_device(int *dev) {
   return hip_check(hipGetDevice(dev), "hipGetDevice");
@@ -59,54 +58,65 @@ int hip_check(hipError_t e, const char *what) {
   return fail(SSM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Returns a workspace holding at least `ntiles` status entries and reserves
-// `ntiles` tickets and a fresh epoch for one launch.
-static int linear_workspace(hipStream_t stream, int64_t ntiles, TileStatus **status,
-                            unsigned long long **ticket, unsigned long long *base,
-                            uint32_t *epoch) {
+// Returns a workspace holding at least `ntiles` status entries and a fresh
+// epoch for one launch, plus the number of workgroups to launch.
+static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *status,
+                            uint32_t *epoch, int *grid) {
   int dev = 0;
   if (int rc = current_device(&dev)) return rc;
   std::lock_guard<std::mutex> lock(g_mu);
+  auto git = g_linear_grid.find(dev);
+  if (git == g_linear_grid.end()) {
+    int cus = 0;
+    if (int rc = hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                                                 dev), "hipDeviceGetAttribute"))
+      return rc;
+    int per_cu = linear_wgs_per_cu();
+    if (per_cu <= 0) return fail(SSM_ERR_HIP, "occupancy query for the scan kernel failed");
+    if (const char *env = getenv("SSMSCAN_LINEAR_WGS_PER_CU")) {
+      const int v = atoi(env);
+      if (v > 0 && v < per_cu) per_cu = v;
+    }
+    git = g_linear_grid.emplace(dev, cus * per_cu).first;
+  }
+  *grid = git->second;
   LinearWorkspace &ws = g_linear[Key(dev, stream)];
+  auto words_for = [](int64_t cap) { return cap + cap / 64 + cap / 4096; };
   if (ws.capacity < ntiles) {
-    if (ws.status) {
-      // The old buffers may still be read by launches queued on this stream.
+    if (ws.words) {
+      // The old buffer may still be read by launches queued on this stream.
       if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
-      (void)hipFree(ws.status);
-      ws.status = nullptr;
-      ws.ticket = nullptr;
+      (void)hipFree(ws.words);
+      ws.words = nullptr;
       ws.capacity = 0;
     }
-    int64_t cap = 1024;
+    int64_t cap = 4096;
     while (cap < ntiles) cap *= 2;
-    const size_t bytes = size_t(cap) * sizeof(TileStatus) + 256;
+    const size_t bytes = size_t(words_for(cap)) * sizeof(AggWord);
     void *p = nullptr;
     if (hipMalloc(&p, bytes) != hipSuccess)
       return fail(SSM_ERR_ALLOC, "hipMalloc of the linear-scan workspace failed");
-    // Zero = epoch 0 everywhere (never written) and a ticket counter of 0.
+    // Zero = epoch 0 everywhere: never written.
     if (int rc = hip_check(hipMemsetAsync(p, 0, bytes, stream), "hipMemsetAsync")) {
       (void)hipFree(p);
       return rc;
     }
-    ws.status = static_cast<TileStatus *>(p);
-    ws.ticket = reinterpret_cast<unsigned long long *>(static_cast<char *>(p) +
-                                                       size_t(cap) * sizeof(TileStatus));
+    ws.words = static_cast<AggWord *>(p);
     ws.capacity = cap;
-    ws.ticket_next = 0;
   }
   if (ws.epoch == 0xffffffffu) {
     // Epochs are about to wrap: make every old word unambiguous again.
-    if (int rc = hip_check(hipMemsetAsync(ws.status, 0, size_t(ws.capacity) * sizeof(TileStatus),
+    if (int rc = hip_check(hipMemsetAsync(ws.words, 0,
+                                          size_t(words_for(ws.capacity)) * sizeof(AggWord),
                                           stream), "hipMemsetAsync"))
       return rc;
     ws.epoch = 0;
   }
   ws.epoch += 1;
-  *status = ws.status;
-  *ticket = ws.ticket;
-  *base = ws.ticket_next;
+  status->lvl0 = ws.words;
+  status->lvl1 = ws.words + ws.capacity;
+  status->lvl2 = ws.words + ws.capacity + ws.capacity / 64;
   *epoch = ws.epoch;
-  ws.ticket_next += (unsigned long long)ntiles;
   return SSM_OK;
 }
 
@@ -167,14 +177,14 @@ int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t 
     return fail(SSM_ERR_INVALID_ARG, "a, b and h must be 16-byte aligned");
   const int64_t tile = linear_tile_elems();
   const int64_t ntiles = (n + tile - 1) / tile;
-  if (ntiles > (int64_t(1) << 31) / 256)
-    return fail(SSM_ERR_UNSUPPORTED, "n too large for one launch");
-  TileStatus *status = nullptr;
-  unsigned long long *ticket = nullptr, base = 0;
+  if (ntiles > kLinearMaxTiles)
+    return fail(SSM_ERR_UNSUPPORTED, "n too large for one launch (max 2^31 elements)");
+  LinearStatus status{};
   uint32_t epoch = 0;
+  int grid = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (int rc = linear_workspace(s, ntiles, &status, &ticket, &base, &epoch)) return rc;
-  return hip_check(launch_linear_scan(a, b, h0, h, n, ntiles, status, ticket, base, epoch, s),
+  if (int rc = linear_workspace(s, ntiles, &status, &epoch, &grid)) return rc;
+  return hip_check(launch_linear_scan(a, b, h0, h, n, ntiles, status, epoch, grid, s),
                    "linear_scan launch");
 }
 
@@ -258,10 +268,10 @@ int ssm_release_workspace(void) {
   int saved = 0;
   (void)hipGetDevice(&saved);
   for (auto &kv : g_linear) {
-    if (!kv.second.status) continue;
+    if (!kv.second.words) continue;
     (void)hipSetDevice(kv.first.first);
     if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = SSM_ERR_HIP;
-    (void)hipFree(kv.second.status);
+    (void)hipFree(kv.second.words);
   }
   for (auto &kv : g_s6) {
     if (!kv.second.buf) continue;

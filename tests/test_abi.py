@@ -53,6 +53,9 @@ def test_linear_scan_argument_errors():
     assert lib.ssm_linear_scan(FAKE, FAKE_MISALIGNED, 0.0, FAKE, 5, None) == \
         ssm.SSM_ERR_INVALID_ARG
     assert b"aligned" in lib.ssm_last_error()
+    # beyond three levels of 64 tiles of 8192 elements
+    assert lib.ssm_linear_scan(FAKE, FAKE, 0.0, FAKE, (1 << 31) + 1, None) == \
+        ssm.SSM_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("fn_name", ["ssm_selective_scan_fwd", "ssm_selective_scan_fwd_bf16"])

@@ -33,9 +33,12 @@ def test_linear_n65536_workload():
     assert_close(run(a, b).numpy(), ref, TOL, "linear-n65536")
 
 
-# sizes straddling lane chunks (4), rows (256), waves (1024), tiles (4096)
-EDGE_N = [1, 2, 3, 4, 5, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 4095, 4096,
-          4097, 8191, 8192, 12289, 65537, 100003, 262144 + 77]
+# sizes straddling lane chunks (4), rows (256), waves (2048), tiles (8192),
+# superblocks (64 tiles) and blocks (4096 tiles)
+EDGE_N = [1, 2, 3, 4, 5, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 2047, 2048, 2049,
+          4095, 4096, 8191, 8192, 8193, 12289, 65537, 100003, 262144 + 77,
+          64 * 8192 - 1, 64 * 8192, 64 * 8192 + 1, 65 * 8192 + 3,
+          4096 * 8192 - 1, 4096 * 8192 + 5]
 
 
 @pytest.mark.parametrize("n", EDGE_N)
@@ -43,7 +46,10 @@ def test_linear_edge_sizes(n):
     say(f"linear edge n={n}")
     a, b = linear_inputs(n, seed=500 + n, a_lo=0.5, a_hi=1.0)
     h0 = 0.75
-    ref = oracle.linear_scan(a.numpy(), b.numpy(), h0)
+    if n > 1_000_000:
+        ref = native.linear_scan(a.numpy(), b.numpy(), h0)
+    else:
+        ref = oracle.linear_scan(a.numpy(), b.numpy(), h0)
     assert_close(run(a, b, h0).numpy(), ref, TOL, f"n={n}")
 
 
@@ -64,7 +70,7 @@ def test_linear_prefix_sum_exact():
     """a == 1 with small integer b: every partial sum is an integer below 2^24,
     so any association is exact and the result must equal the prefix sum."""
     say("linear a=1 integer prefix sum, exact")
-    n = 1 << 20
+    n = 2 * 1024 * 1024 - 3
     g = torch.Generator().manual_seed(5)
     b = torch.randint(-8, 9, (n,), generator=g).float()
     a = torch.ones(n)
