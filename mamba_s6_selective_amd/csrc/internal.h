@@ -32,6 +32,7 @@ struct LinearStatus {
   AggWord *lvl0;
   AggWord *lvl1;
   AggWord *lvl2;
+  unsigned long long *ticket;  // two counters; launch e claims from ticket[e & 1]
 };
 
 // Largest tile count one launch supports (three levels of 64).
@@ -40,10 +41,10 @@ constexpr int64_t kLinearMaxTiles = int64_t(64) * 64 * 64;
 // Elements per tile of the look-back scan.
 int64_t linear_tile_elems();
 
-// Enqueues the single-pass scan as a cooperative launch of
-// min(ntiles, resident_wgs) persistent workgroups. The status levels must hold
-// ntiles, ceil(ntiles/64) and ceil(ntiles/4096) entries whose epochs differ
-// from `epoch`.
+// Enqueues the single-pass scan on min(ntiles, resident_wgs) persistent
+// workgroups. The status levels must hold ntiles, ceil(ntiles/64) and
+// ceil(ntiles/4096) entries whose epochs differ from `epoch`, and
+// ticket[epoch & 1] must be zero.
 hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h,
                               int64_t n, int64_t ntiles, LinearStatus status, uint32_t epoch,
                               int resident_wgs, hipStream_t stream);

@@ -109,6 +109,36 @@ constexpr int kPrefetch = 8;  // steps of u/delta (and y) kept in flight per lan
 // in h and the sum of delta in S. Per-lane words for the next kPrefetch steps
 // are loaded ahead in a register ring; B[t] and C[t] are wave-uniform scalar
 // loads.
+// One step of the chunk-local recurrence for one lane: returns y's value.
+template <typename T, int NT>
+__device__ __forceinline__ float s6_step(float dt, float x, const T *__restrict__ Brow,
+                                         const T *__restrict__ Crow, const float (&Ap)[NT],
+                                         float Dd, float (&h)[NT]) {
+  float Bt[NT], Ct[NT];
+  load_row<NT>(Brow, Bt);
+  load_row<NT>(Crow, Ct);
+  const float du = dt * x;
+  // Two partial sums halve the dependent chain of output FMAs.
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const float dA = exp2_hw(dt * Ap[n]);
+    h[n] = __builtin_fmaf(dA, h[n], du * Bt[n]);
+    if (n & 1)
+      acc1 = __builtin_fmaf(Ct[n], h[n], acc1);
+    else
+      acc0 = __builtin_fmaf(Ct[n], h[n], acc0);
+  }
+  return __builtin_fmaf(Dd, x, acc0 + acc1);
+}
+
+// One sweep of the chunk-local recurrence from a zero state. Writes (or, when
+// Accumulate, adds) y for every step of the chunk and leaves the final state
+// in h and the sum of delta in S. Steps run in blocks of kPrefetch with no
+// branch inside a block (so the compiler can overlap neighbouring steps), and
+// each lane's words for the next block are loaded while the current block
+// computes; B[t] and C[t] are wave-uniform scalar loads. A tail of fewer than
+// kPrefetch steps runs one step at a time.
 template <typename T, int NT, bool Reverse, bool Accumulate>
 __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__restrict__ delta,
                                             const T *__restrict__ B, const T *__restrict__ C,
@@ -120,53 +150,56 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
   S = 0.0f;
   const size_t row0 = size_t(b) * g.L;
   const int len = t1 - t0;
-  // Wave-uniform offset of step i's (b, t, 0) element; the lane adds d.
-  auto row = [&](int i) {
-    const int t = Reverse ? (t1 - 1 - i) : (t0 + i);
-    return (row0 + t) * size_t(g.d_inner);
-  };
+  const int full = len - len % kPrefetch;
+  auto tof = [&](int i) { return Reverse ? (t1 - 1 - i) : (t0 + i); };
+  auto row = [&](int i) { return (row0 + tof(i)) * size_t(g.d_inner); };
   const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));  // input byte offset of the lane
   const uint32_t yo = uint32_t(d) * 4u;                    // output byte offset of the lane
   float rd[kPrefetch], rx[kPrefetch], ry[kPrefetch];
+  if (full > 0) {
 #pragma unroll
-  for (int j = 0; j < kPrefetch; ++j) {
-    if (j < len) {
+    for (int j = 0; j < kPrefetch; ++j) {
       const size_t r = row(j);
       rd[j] = ldv(&at(delta + r, io));
       rx[j] = ldv(&at(u + r, io));
       if (Accumulate) ry[j] = at(y + r, yo);
     }
   }
-  for (int i0 = 0; i0 < len; i0 += kPrefetch) {
+  for (int i0 = 0; i0 < full; i0 += kPrefetch) {
+    float cd[kPrefetch], cx[kPrefetch], cy[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      const int i = i0 + j;
-      if (i < len) {
-        const float dt = rd[j], x = rx[j];
-        const float yprev = Accumulate ? ry[j] : 0.0f;
-        if (i + kPrefetch < len) {
-          const size_t rn = row(i + kPrefetch);
-          rd[j] = ldv(&at(delta + rn, io));
-          rx[j] = ldv(&at(u + rn, io));
-          if (Accumulate) ry[j] = at(y + rn, yo);
-        }
-        const int t = Reverse ? (t1 - 1 - i) : (t0 + i);
-        float Bt[NT], Ct[NT];
-        load_row<NT>(B + (row0 + t) * NT, Bt);
-        load_row<NT>(C + (row0 + t) * NT, Ct);
-        const float du = dt * x;
-        float acc = 0.0f;
+      cd[j] = rd[j];
+      cx[j] = rx[j];
+      if (Accumulate) cy[j] = ry[j];
+    }
+    if (i0 + kPrefetch < full) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const float dA = exp2_hw(dt * Ap[n]);
-          h[n] = __builtin_fmaf(dA, h[n], du * Bt[n]);
-          acc = __builtin_fmaf(Ct[n], h[n], acc);
-        }
-        const float out = __builtin_fmaf(Dd, x, acc);
-        at(y + row(i), yo) = Accumulate ? yprev + out : out;
-        S += dt;
+      for (int j = 0; j < kPrefetch; ++j) {
+        const size_t rn = row(i0 + kPrefetch + j);
+        rd[j] = ldv(&at(delta + rn, io));
+        rx[j] = ldv(&at(u + rn, io));
+        if (Accumulate) ry[j] = at(y + rn, yo);
       }
     }
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+      const int t = tof(i0 + j);
+      const float out = s6_step<T, NT>(cd[j], cx[j], B + (row0 + t) * NT, C + (row0 + t) * NT,
+                                       Ap, Dd, h);
+      at(y + row(i0 + j), yo) = Accumulate ? cy[j] + out : out;
+      S += cd[j];
+    }
+  }
+  for (int i = full; i < len; ++i) {
+    const size_t r = row(i);
+    const float dt = ldv(&at(delta + r, io));
+    const float x = ldv(&at(u + r, io));
+    const int t = tof(i);
+    const float out = s6_step<T, NT>(dt, x, B + (row0 + t) * NT, C + (row0 + t) * NT, Ap, Dd, h);
+    float &yr = at(y + r, yo);
+    yr = Accumulate ? yr + out : out;
+    S += dt;
   }
 }
 
@@ -259,6 +292,24 @@ __global__ __launch_bounds__(kThreads) void s6_carry_kernel(
   }
 }
 
+// Carry contribution at one step: sum_n C[t,n] * cin[n] * exp(A[n] * S).
+template <typename T, int NT>
+__device__ __forceinline__ float fix_step(float S, const T *__restrict__ Crow,
+                                          const float (&Ap)[NT], const float (&cin)[NT]) {
+  float Ct[NT];
+  load_row<NT>(Crow, Ct);
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const float v = cin[n] * exp2_hw(Ap[n] * S);
+    if (n & 1)
+      acc1 = __builtin_fmaf(Ct[n], v, acc1);
+    else
+      acc0 = __builtin_fmaf(Ct[n], v, acc0);
+  }
+  return acc0 + acc1;
+}
+
 template <typename T, int NT, bool Reverse>
 __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *__restrict__ C,
                                           float *__restrict__ y, const float (&Ap)[NT],
@@ -266,42 +317,47 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
                                           int d, int t0, int t1) {
   const size_t row0 = size_t(b) * g.L;
   const int len = t1 - t0;
-  auto row = [&](int i) {
-    const int t = Reverse ? (t1 - 1 - i) : (t0 + i);
-    return (row0 + t) * size_t(g.d_inner);
-  };
+  const int full = len - len % kPrefetch;
+  auto tof = [&](int i) { return Reverse ? (t1 - 1 - i) : (t0 + i); };
+  auto row = [&](int i) { return (row0 + tof(i)) * size_t(g.d_inner); };
   const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));
   const uint32_t yo = uint32_t(d) * 4u;
   float rd[kPrefetch], ry[kPrefetch];
+  if (full > 0) {
 #pragma unroll
-  for (int j = 0; j < kPrefetch; ++j) {
-    if (j < len) {
+    for (int j = 0; j < kPrefetch; ++j) {
       rd[j] = ldv(&at(delta + row(j), io));
       ry[j] = at(y + row(j), yo);
     }
   }
   float S = 0.0f;
-  for (int i0 = 0; i0 < len; i0 += kPrefetch) {
+  for (int i0 = 0; i0 < full; i0 += kPrefetch) {
+    float cd[kPrefetch], cy[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      const int i = i0 + j;
-      if (i < len) {
-        S += rd[j];
-        const float yprev = ry[j];
-        if (i + kPrefetch < len) {
-          rd[j] = ldv(&at(delta + row(i + kPrefetch), io));
-          ry[j] = at(y + row(i + kPrefetch), yo);
-        }
-        const int t = Reverse ? (t1 - 1 - i) : (t0 + i);
-        float Ct[NT];
-        load_row<NT>(C + (row0 + t) * NT, Ct);
-        float acc = 0.0f;
+      cd[j] = rd[j];
+      cy[j] = ry[j];
+    }
+    if (i0 + kPrefetch < full) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-          acc = __builtin_fmaf(Ct[n], cin[n] * exp2_hw(Ap[n] * S), acc);
-        at(y + row(i), yo) = yprev + acc;
+      for (int j = 0; j < kPrefetch; ++j) {
+        rd[j] = ldv(&at(delta + row(i0 + kPrefetch + j), io));
+        ry[j] = at(y + row(i0 + kPrefetch + j), yo);
       }
     }
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+      S += cd[j];
+      const int t = tof(i0 + j);
+      at(y + row(i0 + j), yo) = cy[j] + fix_step<T, NT>(S, C + (row0 + t) * NT, Ap, cin);
+    }
+  }
+  for (int i = full; i < len; ++i) {
+    const size_t r = row(i);
+    S += ldv(&at(delta + r, io));
+    const int t = tof(i);
+    float &yr = at(y + r, yo);
+    yr = yr + fix_step<T, NT>(S, C + (row0 + t) * NT, Ap, cin);
   }
 }
 

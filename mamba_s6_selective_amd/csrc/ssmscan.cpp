@@ -24,7 +24,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Workspace of the look-back linear scan for one (device, stream): the tile
 // status words. Never reset between launches: each launch uses a fresh epoch.
 struct LinearWorkspace {
-  AggWord *words = nullptr;  // capacity + capacity/64 + capacity/4096 entries
+  AggWord *words = nullptr;  // tickets and the three status levels (see linear_workspace)
   int64_t capacity = 0;      // tiles
   uint32_t epoch = 0;        // epoch of the last launch (0 = never)
 };
@@ -81,7 +81,11 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
   }
   *grid = git->second;
   LinearWorkspace &ws = g_linear[Key(dev, stream)];
-  auto words_for = [](int64_t cap) { return cap + cap / 64 + cap / 4096; };
+  // Layout (each part 256-byte aligned so that the polled status words and
+  // the contended ticket counters never share a cache line):
+  //   [2 tickets][level 0: cap][level 1: cap/64][level 2: cap/4096] entries.
+  auto pad = [](int64_t entries) { return (entries * int64_t(sizeof(AggWord)) + 255) / 256 * 256; };
+  auto bytes_for = [&](int64_t cap) { return 256 + pad(cap) + pad(cap / 64) + pad(cap / 4096); };
   if (ws.capacity < ntiles) {
     if (ws.words) {
       // The old buffer may still be read by launches queued on this stream.
@@ -92,11 +96,11 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
     }
     int64_t cap = 4096;
     while (cap < ntiles) cap *= 2;
-    const size_t bytes = size_t(words_for(cap)) * sizeof(AggWord);
+    const size_t bytes = size_t(bytes_for(cap));
     void *p = nullptr;
     if (hipMalloc(&p, bytes) != hipSuccess)
       return fail(SSM_ERR_ALLOC, "hipMalloc of the linear-scan workspace failed");
-    // Zero = epoch 0 everywhere: never written.
+    // Zero = epoch 0 everywhere (never written) and both tickets at 0.
     if (int rc = hip_check(hipMemsetAsync(p, 0, bytes, stream), "hipMemsetAsync")) {
       (void)hipFree(p);
       return rc;
@@ -106,16 +110,17 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
   }
   if (ws.epoch == 0xffffffffu) {
     // Epochs are about to wrap: make every old word unambiguous again.
-    if (int rc = hip_check(hipMemsetAsync(ws.words, 0,
-                                          size_t(words_for(ws.capacity)) * sizeof(AggWord),
-                                          stream), "hipMemsetAsync"))
+    if (int rc = hip_check(hipMemsetAsync(ws.words, 0, size_t(bytes_for(ws.capacity)), stream),
+                           "hipMemsetAsync"))
       return rc;
     ws.epoch = 0;
   }
   ws.epoch += 1;
-  status->lvl0 = ws.words;
-  status->lvl1 = ws.words + ws.capacity;
-  status->lvl2 = ws.words + ws.capacity + ws.capacity / 64;
+  char *base = reinterpret_cast<char *>(ws.words);
+  status->ticket = reinterpret_cast<unsigned long long *>(base);
+  status->lvl0 = reinterpret_cast<AggWord *>(base + 256);
+  status->lvl1 = reinterpret_cast<AggWord *>(base + 256 + pad(ws.capacity));
+  status->lvl2 = reinterpret_cast<AggWord *>(base + 256 + pad(ws.capacity) + pad(ws.capacity / 64));
   *epoch = ws.epoch;
   return SSM_OK;
 }
