@@ -1,0 +1,121 @@
+"""Summaries of rocprofv3 output databases (rocpd SQLite) for profiles/.
+
+    python -m mamba_s6_selective_amd.rocprof_summary stats RUN_results.db ...
+        per-kernel call count and average / total duration (kernel trace)
+
+    python -m mamba_s6_selective_amd.rocprof_summary traffic \\
+        --fetch FETCH_results.db --write WRITE_results.db \\
+        --kernel linear_scan_kernel --copy-bytes 1073741824 --source linear_scan.hip \\
+        --out profiles/linear_scan_traffic.json
+        HBM bytes per launch of a kernel from two counter runs (FETCH_SIZE, then
+        WRITE_SIZE, both in KiB per dispatch), each scaled by the ratio of the
+        bytes the copy kernel moves (copy_bytes read, copy_bytes written) to
+        what the same counter reads for it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import sqlite3
+import statistics
+import sys
+from collections import defaultdict
+from pathlib import Path
+
+CSRC = Path(__file__).resolve().parent / "csrc"
+COPY_KERNEL = "copy_kernel"
+
+
+def short_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
+
+
+def kernel_stats(db: str):
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, total_calls, total_duration, average from top_kernels")
+    return [(short_name(n), int(c), float(t), float(a)) for n, c, t, a in rows]
+
+
+def counter_per_dispatch(db: str, counter: str):
+    """{kernel short name: [value per dispatch]} for one counter."""
+    con = sqlite3.connect(db)
+    acc = defaultdict(float)
+    names = {}
+    for kname, disp, cname, val in con.execute(
+            "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+        if cname != counter:
+            continue
+        acc[disp] += float(val)
+        names[disp] = short_name(kname)
+    out = defaultdict(list)
+    for disp, v in sorted(acc.items()):
+        out[names[disp]].append(v)
+    return out
+
+
+def source_sha(*files: str) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update((CSRC / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def cmd_stats(args):
+    print(f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'total_us':>12}")
+    for db in args.dbs:
+        for name, calls, total, avg in kernel_stats(db):
+            print(f"{name[:60]:<60} {calls:>6} {avg:>10.2f} {total:>12.1f}")
+
+
+def pick(d, key):
+    hits = [k for k in d if key in k]
+    if not hits:
+        raise SystemExit(f"no dispatches of a kernel matching {key!r}: {sorted(d)}")
+    return d[hits[0]]
+
+
+def cmd_traffic(args):
+    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE")
+    write = counter_per_dispatch(args.write, "WRITE_SIZE")
+    kf = statistics.median(pick(fetch, args.kernel))
+    kw = statistics.median(pick(write, args.kernel))
+    cf = statistics.median(pick(fetch, COPY_KERNEL))
+    cw = statistics.median(pick(write, COPY_KERNEL))
+    f_scale = args.copy_bytes / (cf * 1024.0)
+    w_scale = args.copy_bytes / (cw * 1024.0)
+    rec = {
+        "kernel": args.kernel,
+        "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+        "copy_bytes": args.copy_bytes,
+        "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "bytes_per_launch": kf * 1024.0 * f_scale + kw * 1024.0 * w_scale,
+        "kernel_source_sha": source_sha(args.source),
+    }
+    text = json.dumps(rec, indent=1)
+    if args.out:
+        Path(args.out).write_text(text + "\n")
+    print(text)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dbs", nargs="+")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--out")
+    args = ap.parse_args(argv)
+    {"stats": cmd_stats, "traffic": cmd_traffic}[args.cmd](args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
