@@ -47,6 +47,14 @@ __device__ __forceinline__ float ldv(const uint16_t *p) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Waits for every outstanding scalar (and LDS) load. Scalar loads may return
+// out of order, so a wait for one row is a wait for all; issuing it before the
+// next step's row loads (rather than letting the compiler place it after them)
+// keeps those loads in flight across the step.
+__device__ __forceinline__ void wait_scalar_loads() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0 (GFX9 encoding)
+}
+
 // Element at a wave-uniform base plus a per-lane 32-bit byte offset: lets the
 // compiler use the scalar-base + 32-bit-offset form of global loads/stores
 // instead of per-lane 64-bit address arithmetic on the VALU.
@@ -59,28 +67,40 @@ __device__ __forceinline__ const T &at(const T *base, uint32_t byte_off) {
   return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
-// Loads the N-long row p[0..NT) (wave-uniform address) as fp32. bf16 rows of
-// even length are read as 32-bit words so that the loads stay scalar and the
-// widening to fp32 (a shift or a mask) runs on the scalar unit.
-template <int NT>
-__device__ __forceinline__ void load_row(const float *__restrict__ p, float (&out)[NT]) {
+// A B or C row (N values at a wave-uniform address) as raw words, so it can
+// be loaded one step ahead into SGPRs and widened to fp32 only when used. bf16
+// rows of even length are read as 32-bit words (two values each); the loads
+// stay scalar and the widening (a shift or a mask) runs on the scalar unit.
+template <typename T, int NT>
+struct Row {
+  static constexpr bool kPacked = sizeof(T) == 2 && NT % 2 == 0;
+  static constexpr int kWords = kPacked ? NT / 2 : NT;
+  uint32_t w[kWords];
+
+  __device__ __forceinline__ void load(const T *__restrict__ p) {
+    if constexpr (sizeof(T) == 4 || kPacked) {
+      const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
 #pragma unroll
-  for (int n = 0; n < NT; ++n) out[n] = p[n];
-}
-template <int NT>
-__device__ __forceinline__ void load_row(const uint16_t *__restrict__ p, float (&out)[NT]) {
-  if constexpr (NT % 2 == 0) {
-    const uint32_t *w = reinterpret_cast<const uint32_t *>(p);
+      for (int i = 0; i < kWords; ++i) w[i] = q[i];
+    } else {
 #pragma unroll
-    for (int i = 0; i < NT / 2; ++i) {
-      const uint32_t v = w[i];
-      out[2 * i] = __uint_as_float(v << 16);
-      out[2 * i + 1] = __uint_as_float(v & 0xffff0000u);
+      for (int i = 0; i < kWords; ++i) w[i] = uint32_t(p[i]) << 16;
     }
-  } else {
-#pragma unroll
-    for (int n = 0; n < NT; ++n) out[n] = ldv(p + n);
   }
+  __device__ __forceinline__ float get(int n) const {
+    if constexpr (kPacked)
+      return __uint_as_float((n & 1) ? (w[n >> 1] & 0xffff0000u) : (w[n >> 1] << 16));
+    else
+      return __uint_as_float(w[n]);
+  }
+};
+
+template <typename T, int NT>
+__device__ __forceinline__ void load_row(const T *__restrict__ p, float (&out)[NT]) {
+  Row<T, NT> r;
+  r.load(p);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) out[n] = r.get(n);
 }
 
 struct Geometry {
@@ -104,30 +124,22 @@ __device__ __forceinline__ size_t agg_index(const Geometry &g, int NT, int b, in
 
 constexpr int kPrefetch = 8;  // steps of u/delta (and y) kept in flight per lane
 
-// One sweep of the chunk-local recurrence from a zero state. Writes (or, when
-// Accumulate, adds) y for every step of the chunk and leaves the final state
-// in h and the sum of delta in S. Per-lane words for the next kPrefetch steps
-// are loaded ahead in a register ring; B[t] and C[t] are wave-uniform scalar
-// loads.
 // One step of the chunk-local recurrence for one lane: returns y's value.
 template <typename T, int NT>
-__device__ __forceinline__ float s6_step(float dt, float x, const T *__restrict__ Brow,
-                                         const T *__restrict__ Crow, const float (&Ap)[NT],
+__device__ __forceinline__ float s6_step(float dt, float x, const Row<T, NT> &Br,
+                                         const Row<T, NT> &Cr, const float (&Ap)[NT],
                                          float Dd, float (&h)[NT]) {
-  float Bt[NT], Ct[NT];
-  load_row<NT>(Brow, Bt);
-  load_row<NT>(Crow, Ct);
   const float du = dt * x;
   // Two partial sums halve the dependent chain of output FMAs.
   float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const float dA = exp2_hw(dt * Ap[n]);
-    h[n] = __builtin_fmaf(dA, h[n], du * Bt[n]);
+    h[n] = __builtin_fmaf(dA, h[n], du * Br.get(n));
     if (n & 1)
-      acc1 = __builtin_fmaf(Ct[n], h[n], acc1);
+      acc1 = __builtin_fmaf(Cr.get(n), h[n], acc1);
     else
-      acc0 = __builtin_fmaf(Ct[n], h[n], acc0);
+      acc0 = __builtin_fmaf(Cr.get(n), h[n], acc0);
   }
   return __builtin_fmaf(Dd, x, acc0 + acc1);
 }
@@ -182,13 +194,25 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
         if (Accumulate) ry[j] = at(y + rn, yo);
       }
     }
+    // B/C rows go one step ahead: step j's rows were loaded during step j-1.
+    Row<T, NT> Bc, Cc;
+    Bc.load(B + (row0 + tof(i0)) * NT);
+    Cc.load(C + (row0 + tof(i0)) * NT);
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      const int t = tof(i0 + j);
-      const float out = s6_step<T, NT>(cd[j], cx[j], B + (row0 + t) * NT, C + (row0 + t) * NT,
-                                       Ap, Dd, h);
+      Row<T, NT> Bn, Cn;
+      wait_scalar_loads();
+      if (j + 1 < kPrefetch) {
+        Bn.load(B + (row0 + tof(i0 + j + 1)) * NT);
+        Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
+      }
+      const float out = s6_step<T, NT>(cd[j], cx[j], Bc, Cc, Ap, Dd, h);
       at(y + row(i0 + j), yo) = Accumulate ? cy[j] + out : out;
       S += cd[j];
+      if (j + 1 < kPrefetch) {
+        Bc = Bn;
+        Cc = Cn;
+      }
     }
   }
   for (int i = full; i < len; ++i) {
@@ -196,7 +220,10 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
     const float dt = ldv(&at(delta + r, io));
     const float x = ldv(&at(u + r, io));
     const int t = tof(i);
-    const float out = s6_step<T, NT>(dt, x, B + (row0 + t) * NT, C + (row0 + t) * NT, Ap, Dd, h);
+    Row<T, NT> Bc, Cc;
+    Bc.load(B + (row0 + t) * NT);
+    Cc.load(C + (row0 + t) * NT);
+    const float out = s6_step<T, NT>(dt, x, Bc, Cc, Ap, Dd, h);
     float &yr = at(y + r, yo);
     yr = Accumulate ? yr + out : out;
     S += dt;
@@ -294,18 +321,16 @@ __global__ __launch_bounds__(kThreads) void s6_carry_kernel(
 
 // Carry contribution at one step: sum_n C[t,n] * cin[n] * exp(A[n] * S).
 template <typename T, int NT>
-__device__ __forceinline__ float fix_step(float S, const T *__restrict__ Crow,
-                                          const float (&Ap)[NT], const float (&cin)[NT]) {
-  float Ct[NT];
-  load_row<NT>(Crow, Ct);
+__device__ __forceinline__ float fix_step(float S, const Row<T, NT> &Cr, const float (&Ap)[NT],
+                                          const float (&cin)[NT]) {
   float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const float v = cin[n] * exp2_hw(Ap[n] * S);
     if (n & 1)
-      acc1 = __builtin_fmaf(Ct[n], v, acc1);
+      acc1 = __builtin_fmaf(Cr.get(n), v, acc1);
     else
-      acc0 = __builtin_fmaf(Ct[n], v, acc0);
+      acc0 = __builtin_fmaf(Cr.get(n), v, acc0);
   }
   return acc0 + acc1;
 }
@@ -345,19 +370,25 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
         ry[j] = at(y + row(i0 + kPrefetch + j), yo);
       }
     }
+    Row<T, NT> Cc;
+    Cc.load(C + (row0 + tof(i0)) * NT);
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
+      Row<T, NT> Cn;
+      wait_scalar_loads();
+      if (j + 1 < kPrefetch) Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
       S += cd[j];
-      const int t = tof(i0 + j);
-      at(y + row(i0 + j), yo) = cy[j] + fix_step<T, NT>(S, C + (row0 + t) * NT, Ap, cin);
+      at(y + row(i0 + j), yo) = cy[j] + fix_step<T, NT>(S, Cc, Ap, cin);
+      if (j + 1 < kPrefetch) Cc = Cn;
     }
   }
   for (int i = full; i < len; ++i) {
     const size_t r = row(i);
     S += ldv(&at(delta + r, io));
-    const int t = tof(i);
+    Row<T, NT> Cc;
+    Cc.load(C + (row0 + tof(i)) * NT);
     float &yr = at(y + r, yo);
-    yr = yr + fix_step<T, NT>(S, C + (row0 + t) * NT, Ap, cin);
+    yr = yr + fix_step<T, NT>(S, Cc, Ap, cin);
   }
 }
 
