@@ -16,11 +16,12 @@
 //
 // The sequence is split into chunks so that enough lanes run (L-splitting):
 //  1. chunk pass: every chunk runs its recurrence from a zero state, writes
-//     its local y (with the D*u term) and its aggregate affine map per (d, n):
-//     multiplier exp(A*sum(delta)) and the local end state (reverse: the local
-//     state at the chunk start).
-//  2. carry pass: per (b, n, d), a sequential left fold over the chunk
-//     aggregates gives each chunk's incoming state (forward and/or reverse).
+//     its local y (with the D*u term), the sum of delta over the chunk per d
+//     (the chunk's multiplier for state n is exp(A[d,n] * that sum)) and the
+//     local end state per (d, n) (reverse: the local state at the chunk start).
+//  2. carry pass: per (b, n, d), a left fold over the chunk aggregates gives
+//     each chunk's incoming state (forward and/or reverse); the fold is split
+//     over waves (parts of up to 32 chunks) joined through LDS.
 //  3. fix pass: every chunk except the first (forward) / last (reverse) adds
 //     sum_n C[t,n] * carry_n * exp(A_n * S_t), S_t the running sum of delta
 //     from the carry's entry point, to its y. This is the exact carry
@@ -116,10 +117,14 @@ __device__ __forceinline__ void decompose(const Geometry &g, int &b, int &c, int
   d = grp * kThreads + threadIdx.x;
 }
 
-// Aggregate / carry arrays are laid out [b][chunk][n][d] so lanes (d) are contiguous.
+// End-state / carry arrays are laid out [b][chunk][n][d] and delta sums
+// [b][chunk][d], so lanes (d) are contiguous.
 __device__ __forceinline__ size_t agg_index(const Geometry &g, int NT, int b, int c, int n,
                                             int d) {
   return ((size_t(b) * g.nchunks + c) * NT + n) * g.d_inner + d;
+}
+__device__ __forceinline__ size_t sum_index(const Geometry &g, int b, int c, int d) {
+  return (size_t(b) * g.nchunks + c) * g.d_inner + d;
 }
 
 constexpr int kPrefetch = 8;  // steps of u/delta (and y) kept in flight per lane
@@ -234,7 +239,7 @@ template <typename T, int NT>
 __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
     const T *__restrict__ u, const T *__restrict__ delta, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
-    float *__restrict__ y, float *__restrict__ agg_a, float *__restrict__ agg_f,
+    float *__restrict__ y, float *__restrict__ agg_s, float *__restrict__ agg_f,
     float *__restrict__ agg_r, Geometry g, int direction) {
   int b, c, d;
   decompose(g, b, c, d);
@@ -251,11 +256,9 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
   if (direction != SSM_DIR_REV) {
     chunk_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1, h, S);
     if (multi) {
+      agg_s[sum_index(g, b, c, d)] = S;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        agg_a[agg_index(g, NT, b, c, n, d)] = exp2_hw(Ap[n] * S);
-        agg_f[agg_index(g, NT, b, c, n, d)] = h[n];
-      }
+      for (int n = 0; n < NT; ++n) agg_f[agg_index(g, NT, b, c, n, d)] = h[n];
     }
   }
   if (direction != SSM_DIR_FWD) {
@@ -264,58 +267,77 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
     else
       chunk_sweep<T, NT, true, false>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1, h, S);
     if (multi) {
+      if (direction == SSM_DIR_REV) agg_s[sum_index(g, b, c, d)] = S;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        if (direction == SSM_DIR_REV) agg_a[agg_index(g, NT, b, c, n, d)] = exp2_hw(Ap[n] * S);
-        agg_r[agg_index(g, NT, b, c, n, d)] = h[n];
-      }
+      for (int n = 0; n < NT; ++n) agg_r[agg_index(g, NT, b, c, n, d)] = h[n];
     }
   }
 }
 
-// Per (b, n, d): incoming state of every chunk, by a sequential left fold of
-// the chunk aggregates (forward: chunk 0 upwards; reverse: last chunk down).
-// Aggregates are loaded kGroup at a time before being folded, so the loads of
-// a group are in flight together rather than one dependent load per chunk.
-constexpr int kGroup = 16;
+// Per (b, n, d): incoming state of every chunk, by a left fold of the chunk
+// aggregates (forward: chunk 0 upwards; reverse: last chunk down). A block
+// covers 64 channels (lanes) of one (b, n); wave p owns chunks
+// [p*kCarryPart, (p+1)*kCarryPart) in both directions, holds their
+// multipliers and end states in registers, and folds them into part totals;
+// the totals meet in LDS, and each wave then replays its chunks from the fold
+// of the totals before it (forward: lower parts; reverse: higher parts).
+// Fixed shapes, so the result is deterministic.
+constexpr int kCarryPart = 16;
+constexpr int kCarryMaxParts = 16;  // so at most 256 chunks
 
-__global__ __launch_bounds__(kThreads) void s6_carry_kernel(
-    const float *__restrict__ agg_a, const float *__restrict__ agg_f,
-    const float *__restrict__ agg_r, float *__restrict__ carry_f, float *__restrict__ carry_r,
-    Geometry g, int NT, int direction) {
-  const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t per_b = int64_t(NT) * g.d_inner;
-  if (idx >= per_b * g.batch) return;
-  const int b = int(idx / per_b);
-  const int rem = int(idx % per_b);  // n * d_inner + d
-  const size_t stride = size_t(NT) * g.d_inner;
-  const size_t base = size_t(b) * g.nchunks * stride + rem;
-  for (int dir = 0; dir < 2; ++dir) {
-    if (dir == 0 && direction == SSM_DIR_REV) continue;
-    if (dir == 1 && direction == SSM_DIR_FWD) continue;
-    const float *aggb = dir == 0 ? agg_f : agg_r;
-    float *carry = dir == 0 ? carry_f : carry_r;
-    float c = 0.0f;
-    for (int k0 = 0; k0 < g.nchunks; k0 += kGroup) {
-      float ga[kGroup], gb[kGroup];
+__global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
+    const float *__restrict__ agg_s, const float *__restrict__ agg_f,
+    const float *__restrict__ agg_r, const float *__restrict__ A, float *__restrict__ carry_f,
+    float *__restrict__ carry_r, Geometry g, int NT, int direction) {
+  __shared__ float s_a[kCarryMaxParts][64], s_f[kCarryMaxParts][64], s_r[kCarryMaxParts][64];
+  const int lane = threadIdx.x & 63;
+  const int part = threadIdx.x >> 6;
+  const int parts = blockDim.x >> 6;
+  const int dgroups = (g.d_inner + 63) / 64;
+  int bid = blockIdx.x;
+  const int dg = bid % dgroups;
+  bid /= dgroups;
+  const int n = bid % NT;
+  const int b = bid / NT;
+  const int d = dg * 64 + lane;
+  const bool valid = d < g.d_inner;
+  const bool fwd = direction != SSM_DIR_REV, rev = direction != SSM_DIR_FWD;
+  const float Ap = valid ? A[size_t(d) * NT + n] * kLog2e : 0.0f;
+  const int k0 = part * kCarryPart;
+  float ra[kCarryPart], rf[kCarryPart], rr[kCarryPart];
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        const int k = dir == 0 ? k0 + j : g.nchunks - 1 - (k0 + j);
-        if (k0 + j < g.nchunks) {
-          const size_t i = base + size_t(k) * stride;
-          ga[j] = agg_a[i];
-          gb[j] = aggb[i];
-        }
-      }
+  for (int i = 0; i < kCarryPart; ++i) {
+    const int k = k0 + i;
+    const bool in = valid && k < g.nchunks;  // chunks past the end act as identity maps
+    ra[i] = in ? exp2_hw(Ap * agg_s[sum_index(g, b, k, d)]) : 1.0f;
+    rf[i] = in && fwd ? agg_f[agg_index(g, NT, b, k, n, d)] : 0.0f;
+    rr[i] = in && rev ? agg_r[agg_index(g, NT, b, k, n, d)] : 0.0f;
+  }
+  float ta = 1.0f, tf = 0.0f, tr = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        const int k = dir == 0 ? k0 + j : g.nchunks - 1 - (k0 + j);
-        if (k0 + j < g.nchunks) {
-          carry[base + size_t(k) * stride] = c;
-          c = __builtin_fmaf(ga[j], c, gb[j]);
-        }
-      }
-    }
+  for (int i = 0; i < kCarryPart; ++i) {
+    tf = __builtin_fmaf(ra[i], tf, rf[i]);
+    tr = __builtin_fmaf(ra[kCarryPart - 1 - i], tr, rr[kCarryPart - 1 - i]);
+    ta *= ra[i];
+  }
+  s_a[part][lane] = ta;
+  s_f[part][lane] = tf;
+  s_r[part][lane] = tr;
+  __syncthreads();
+  float cf = 0.0f, cr = 0.0f;
+  for (int q = 0; q < part; ++q) cf = __builtin_fmaf(s_a[q][lane], cf, s_f[q][lane]);
+  for (int q = parts - 1; q > part; --q) cr = __builtin_fmaf(s_a[q][lane], cr, s_r[q][lane]);
+#pragma unroll
+  for (int i = 0; i < kCarryPart; ++i) {
+    const int k = k0 + i;
+    if (fwd && valid && k < g.nchunks) carry_f[agg_index(g, NT, b, k, n, d)] = cf;
+    cf = __builtin_fmaf(ra[i], cf, rf[i]);
+  }
+#pragma unroll
+  for (int i = kCarryPart - 1; i >= 0; --i) {
+    const int k = k0 + i;
+    if (rev && valid && k < g.nchunks) carry_r[agg_index(g, NT, b, k, n, d)] = cr;
+    cr = __builtin_fmaf(ra[i], cr, rr[i]);
   }
 }
 
@@ -420,21 +442,41 @@ __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
   }
 }
 
-// Chunk length: enough (batch, chunk, channel-group) workgroups to give every
-// SIMD of the 256 CUs several waves, but never shorter than 16 steps.
-int plan_chunk(int batch, int L, int groups) {
-  if (const char *env = getenv("SSMSCAN_S6_CHUNK")) {
-    const int v = atoi(env);
-    if (v > 0) return v;
+// Chunk length (a multiple of 8): as many (batch, chunk, channel-group)
+// workgroups as the GPU holds at once (one round, so every workgroup starts
+// together and none waits for a second round), chunks of at least 16 steps,
+// at most kCarryPart * kCarryMaxParts chunks per sequence. SSMSCAN_S6_CHUNK
+// overrides the length (still within the chunk-count limit).
+int plan_chunk(int batch, int L, int groups, int resident_wgs) {
+  const int64_t max_chunks = kCarryPart * kCarryMaxParts;
+  int64_t chunk = 0;
+  if (const char *env = getenv("SSMSCAN_S6_CHUNK")) chunk = atoi(env);
+  if (chunk <= 0) {
+    const int64_t rows = int64_t(batch) * groups;
+    int64_t nch = resident_wgs / rows;
+    if (nch < 1) nch = 1;
+    chunk = (L + nch - 1) / nch;
+    if (chunk < 16) chunk = 16;
   }
-  const int64_t target_wgs = 2048;
-  const int64_t rows = int64_t(batch) * groups;
-  int64_t nch = (target_wgs + rows - 1) / rows;
-  if (nch < 1) nch = 1;
-  int64_t chunk = (L + nch - 1) / nch;
-  if (chunk < 16) chunk = 16;
+  if (chunk < (L + max_chunks - 1) / max_chunks) chunk = (L + max_chunks - 1) / max_chunks;
   chunk = (chunk + 7) / 8 * 8;
   return int(chunk);
+}
+
+// Workgroups of the chunk kernel resident on the whole device at once.
+template <typename T, int NT>
+int resident_chunk_wgs() {
+  static int cached = 0;
+  if (cached > 0) return cached;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, s6_chunk_kernel<T, NT>, kThreads,
+                                                   0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0)
+    return 1024;
+  cached = cus * per_cu;
+  return cached;
 }
 
 template <typename T, int NT>
@@ -444,39 +486,41 @@ int launch_all(const S6Args &a, hipStream_t stream) {
   g.L = a.L;
   g.d_inner = a.d_inner;
   g.groups = (a.d_inner + kThreads - 1) / kThreads;
-  g.chunk = plan_chunk(a.batch, a.L, g.groups);
+  g.chunk = plan_chunk(a.batch, a.L, g.groups, resident_chunk_wgs<T, NT>());
   g.nchunks = (a.L + g.chunk - 1) / g.chunk;
   const int64_t wgs = int64_t(g.groups) * g.nchunks * a.batch;
   if (wgs > (int64_t(1) << 31) - 1) return fail(SSM_ERR_UNSUPPORTED, "problem too large");
 
-  float *agg_a = nullptr, *agg_f = nullptr, *agg_r = nullptr, *car_f = nullptr,
+  float *agg_s = nullptr, *agg_f = nullptr, *agg_r = nullptr, *car_f = nullptr,
         *car_r = nullptr;
   if (g.nchunks > 1) {
     const size_t per = size_t(a.batch) * g.nchunks * NT * a.d_inner;
+    const size_t sums = (size_t(a.batch) * g.nchunks * a.d_inner + 63) / 64 * 64;
     void *buf = nullptr;
     unsigned long long *ticket = nullptr, base = 0;
     uint32_t epoch = 0;
-    if (int rc = s6_workspace(stream, 5 * per * sizeof(float), 0, &buf, &ticket, &base, &epoch))
+    if (int rc = s6_workspace(stream, (4 * per + sums) * sizeof(float), 0, &buf, &ticket, &base,
+                              &epoch))
       return rc;
     float *f = static_cast<float *>(buf);
-    agg_a = f;
-    agg_f = f + per;
-    agg_r = f + 2 * per;
-    car_f = f + 3 * per;
-    car_r = f + 4 * per;
+    agg_s = f;
+    agg_f = f + sums;
+    agg_r = agg_f + per;
+    car_f = agg_r + per;
+    car_r = car_f + per;
   }
   const T *u = static_cast<const T *>(a.u);
   const T *dl = static_cast<const T *>(a.delta);
   const T *B = static_cast<const T *>(a.B);
   const T *C = static_cast<const T *>(a.C);
   hipLaunchKernelGGL((s6_chunk_kernel<T, NT>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
-                     u, dl, a.A, B, C, a.D, a.y, agg_a, agg_f, agg_r, g, a.direction);
+                     u, dl, a.A, B, C, a.D, a.y, agg_s, agg_f, agg_r, g, a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 chunk launch")) return rc;
   if (g.nchunks == 1) return SSM_OK;
-  const int64_t lanes = int64_t(a.batch) * NT * a.d_inner;
-  hipLaunchKernelGGL(s6_carry_kernel, dim3(unsigned((lanes + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, stream, agg_a, agg_f, agg_r, car_f, car_r, g, NT,
-                     a.direction);
+  const int parts = (g.nchunks + kCarryPart - 1) / kCarryPart;
+  const int64_t carry_blocks = int64_t(a.batch) * NT * ((a.d_inner + 63) / 64);
+  hipLaunchKernelGGL(s6_carry_kernel, dim3(unsigned(carry_blocks)), dim3(64 * parts), 0, stream,
+                     agg_s, agg_f, agg_r, a.A, car_f, car_r, g, NT, a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 carry launch")) return rc;
   hipLaunchKernelGGL((s6_fix_kernel<T, NT>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream, dl,
                      a.A, C, a.y, car_f, car_r, g, a.direction);
