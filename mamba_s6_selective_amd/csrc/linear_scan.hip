@@ -10,11 +10,11 @@
 // inspection of predecessors. This kernel keeps the single pass, the
 // register-resident items and the wave-wide inspection, and re-plans the
 // cross-tile protocol for a part whose workgroups sit on 8 XCDs with private
-// L2s, where a published word takes on the order of a microsecond to become
-// visible to another XCD:
+// L2s, where a status read that must see other XCDs' writes takes several
+// microseconds while HBM is streaming:
 //
-//  * tile = 4 waves x 8 rows x 64 lanes x float4 = 8192 elements. Each row is
-//    read and written with one fully coalesced 1 KiB global_load/store_dwordx4
+//  * tile = 8 data waves x 4 rows x 64 lanes x float4 = 8192 elements. Each row
+//    is read and written with one fully coalesced 1 KiB global_load/store_dwordx4
 //    per wave (no LDS transpose). Per lane: 4-element chunk aggregates in
 //    registers; per row: a wave64 inclusive scan of chunk aggregates with DPP
 //    row_shr / row_bcast steps; per wave and per tile: short serial folds.
@@ -25,10 +25,10 @@
 //    superblock of 64 tiles (level 1, published by the superblock's last
 //    tile), and that of its block of 64 superblocks (level 2, published by
 //    the block's last tile). A tile's incoming value is h0 pushed through the
-//    composition of at most 63 level-2, 63 level-1 and 63 level-0 aggregates,
-//    each window composed by one fixed-shape wave64 DPP scan. Every wait is on
-//    aggregates that depend only on loads of earlier tiles, so a tile waits a
-//    bounded number of round trips, whatever the size of the input.
+//    composition of level-2, level-1 and level-0 windows of at most 64 words
+//    each, each window composed by one fixed-shape wave64 DPP scan; the most
+//    recent superblocks are read at level 0, so a look-back never waits on
+//    another look-back that runs at the same time.
 //  * deterministic: the window contents and the shape of every composition are
 //    fixed by the tile index alone, so the output is bitwise identical from
 //    run to run.
@@ -40,8 +40,10 @@
 //    a ticket counter, so a tile only ever waits for lower tiles that running
 //    workgroups own, and the lowest unfinished tile can always finish (no
 //    assumption about how many workgroups are resident). Each workgroup has
-//    four data waves, which load the next tile while the current one waits,
-//    and one control wave that claims, publishes and looks back.
+//    eight data waves and one control wave, and a tile moves through a
+//    four-stage pipeline (load, scan and publish, look-back, apply and store)
+//    in which every long-latency step -- a tile's loads, the status reads of
+//    its look-back -- is issued one iteration before its result is used.
 //  * data moves with non-temporal 16-byte loads and stores (read once, written
 //    once), which measured about 8% faster than default caching here.
 #include <hip/hip_runtime.h>
@@ -52,11 +54,11 @@
 namespace ssm {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kRows = 8;
+constexpr int kWaves = 8;
+constexpr int kRows = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowElems = 256;                    // 64 lanes x float4
-constexpr int kWaveElems = kRowElems * kRows;     // 2048
+constexpr int kWaveElems = kRowElems * kRows;     // 1024
 constexpr int kTileElems = kWaveElems * kWaves;   // 8192
 constexpr int kFan = 64;                          // entries per look-back window
 
@@ -137,104 +139,133 @@ __device__ __forceinline__ void window_total(float a, float b, int count, int la
   tb = lane_f(b, 63);
 }
 
-// Composition of the superblocks of this block before the current one: the
-// level-1 words of all but the last (n1_old of them), then the last one
-// composed from its 64 level-0 words (lanes 0..62 by the window scan, lane 63
-// on top) -- the same operations its own last tile performs to publish it.
-__device__ __forceinline__ void superblock_prefix(uint64_t w1a, uint64_t w1b, int n1_old,
-                                                  uint64_t wpa, uint64_t wpb, bool use_prev,
-                                                  int lane, float &pa, float &pb) {
-  window_total(payload(w1a), payload(w1b), n1_old, lane, pa, pb);
-  if (use_prev) {
-    float qa, qb;
-    window_total(payload(wpa), payload(wpb), kFan - 1, lane, qa, qb);
-    const float la = lane_f(payload(wpa), kFan - 1), lb = lane_f(payload(wpb), kFan - 1);
-    const float ta = qa * la, tb = __builtin_fmaf(la, qb, lb);  // previous superblock
-    pb = __builtin_fmaf(ta, pb, tb);
-    pa = pa * ta;
+// Look-back windows at level 0: the tile's own superblock and the
+// kRecent - 1 superblocks before it. Older superblocks are read at level 1 and
+// older blocks at level 2, but the words of those recent superblocks (and of
+// the block they may straddle into) come from look-backs that may still be
+// running when this one starts, so they are composed here from level-0 words.
+constexpr int kRecent = 5;
+
+// Resumable look-back of one tile: which words it reads, the words read so
+// far and, per lane, whether that lane's word is complete. The tile's prefix
+// is  (level-2 words of blocks [0, blk1)) (+) (level-1 words of superblocks
+// [blk1*64, sb0)) (+) (level-0 windows of superblocks sb0 .. sb, the last one
+// cut at the tile).
+struct LookBack {
+  int64_t sb0, blk1;
+  int nw, n0, n1, n2;
+  uint64_t wa[kRecent], wb[kRecent], w1a, w1b, w2a, w2b;
+  bool r[kRecent], r1, r2;
+};
+
+// Prefixes of one tile: P0 over the earlier tiles of its superblock, PB over
+// everything from the start of block blk1 up to its superblock, and h_in
+// (h0 pushed through the level-2 prefix, then PB, then P0).
+struct Prefix {
+  float p0a, p0b, pba, pbb, h_in;
+};
+
+__device__ __forceinline__ void lb_init(LookBack &s, int64_t tile, int lane) {
+  const int64_t sb = tile / kFan;
+  s.n0 = int(tile - sb * kFan);
+  s.sb0 = sb >= kRecent - 1 ? sb - (kRecent - 1) : 0;
+  s.nw = int(sb - s.sb0) + 1;
+  s.blk1 = s.sb0 / kFan;
+  s.n1 = int(s.sb0 - s.blk1 * kFan);
+  s.n2 = int(s.blk1);
+#pragma unroll
+  for (int q = 0; q < kRecent; ++q) {
+    const int entries = q < s.nw - 1 ? kFan : (q == s.nw - 1 ? s.n0 : 0);
+    s.r[q] = !(lane < entries);
+    s.wa[q] = 0;
+    s.wb[q] = 0;
+  }
+  s.r1 = !(lane < s.n1);
+  s.r2 = !(lane < s.n2);
+  s.w1a = s.w1b = s.w2a = s.w2b = 0;
+}
+
+// One round of status reads for the words not yet complete. The loads are
+// only issued here; lb_check reads them, so the reads of two look-backs can
+// be in flight together.
+__device__ __forceinline__ void lb_issue(LookBack &s, const LinearStatus &st, int lane) {
+#pragma unroll
+  for (int q = 0; q < kRecent; ++q) {
+    if (!s.r[q]) {
+      const int64_t i = (s.sb0 + q) * kFan + lane;
+      s.wa[q] = ld_status(&st.lvl0[i].a);
+      s.wb[q] = ld_status(&st.lvl0[i].b);
+    }
+  }
+  if (!s.r1) {
+    s.w1a = ld_status(&st.lvl1[s.blk1 * kFan + lane].a);
+    s.w1b = ld_status(&st.lvl1[s.blk1 * kFan + lane].b);
+  }
+  if (!s.r2) {
+    s.w2a = ld_status(&st.lvl2[lane].a);
+    s.w2b = ld_status(&st.lvl2[lane].b);
   }
 }
 
-// Incoming value of `tile`, composed from published aggregates (see the file
-// comment): P2 over the level-2 words of earlier blocks, P1 over the level-1
-// words of earlier superblocks of this block, P0 over the level-0 words of
-// earlier tiles of this superblock. The superblock just before this one is
-// not read from level 1 (its word is published by its last tile's look-back,
-// one round trip later than its tiles' own words) but composed here from its
-// 64 level-0 words with exactly the arithmetic its last tile uses to publish
-// it, so both give the same bits. The last tile of a superblock publishes the
-// superblock's aggregate, and the last tile of a block the block's aggregate,
-// as soon as their inputs are visible. Called by all 64 lanes of one wave.
-__device__ float look_back(const LinearStatus &st, int64_t tile, float ga, float gb, float h0,
-                           uint32_t epoch, int lane) {
-  const int64_t sb = tile / kFan;             // superblock of this tile
-  const int64_t blk = sb / kFan;              // block of this tile
-  const int n0 = int(tile - sb * kFan);       // level-0 words before the tile in its superblock
-  const int n1 = int(sb - blk * kFan);        // superblocks before this one in its block
-  const int n2 = int(blk);                    // blocks before this one
-  const bool use_prev = n1 > 0;               // previous superblock composed from level 0
-  const int n1_old = use_prev ? n1 - 1 : 0;   // level-1 words read
-  const bool last_in_sb = n0 == kFan - 1;
-  const bool last_in_blk = last_in_sb && n1 == kFan - 1;
-  const int64_t i0 = sb * kFan + lane, ip = (sb - 1) * kFan + lane;
-  const int64_t i1 = blk * kFan + lane, i2 = lane;
-  uint64_t w0a = 0, w0b = 0, wpa = 0, wpb = 0, w1a = 0, w1b = 0, w2a = 0, w2b = 0;
-  bool r0 = !(lane < n0), rp = !use_prev, r1 = !(lane < n1_old), r2 = !(lane < n2);
-  bool pub1 = !last_in_sb, pub2 = !last_in_blk;
-  float sa = 1.0f, sbv = 0.0f;  // this superblock's aggregate, when published here
-  for (;;) {
-    if (!r0) {
-      w0a = ld_status(&st.lvl0[i0].a);
-      w0b = ld_status(&st.lvl0[i0].b);
-      r0 = word_ready(w0a, epoch) && word_ready(w0b, epoch);
+__device__ __forceinline__ void lb_check(LookBack &s, uint32_t epoch) {
+#pragma unroll
+  for (int q = 0; q < kRecent; ++q)
+    s.r[q] = s.r[q] || (word_ready(s.wa[q], epoch) && word_ready(s.wb[q], epoch));
+  s.r1 = s.r1 || (word_ready(s.w1a, epoch) && word_ready(s.w1b, epoch));
+  s.r2 = s.r2 || (word_ready(s.w2a, epoch) && word_ready(s.w2b, epoch));
+}
+
+__device__ __forceinline__ bool lb_done(const LookBack &s) {
+  bool pending = __ballot(!s.r1) != 0 || __ballot(!s.r2) != 0;
+#pragma unroll
+  for (int q = 0; q < kRecent; ++q) pending = pending || __ballot(!s.r[q]) != 0;
+  return !pending;
+}
+
+// Composition of the complete look-back windows (fixed shapes: the result
+// depends only on the words and the tile index).
+__device__ Prefix lb_finish(const LookBack &s, float h0, int lane) {
+  float p2a, p2b, pba, pbb;
+  window_total(payload(s.w2a), payload(s.w2b), s.n2, lane, p2a, p2b);
+  window_total(payload(s.w1a), payload(s.w1b), s.n1, lane, pba, pbb);
+  Prefix pf;
+#pragma unroll
+  for (int q = 0; q < kRecent; ++q) {
+    if (q < s.nw - 1) {  // a whole earlier superblock
+      float qa, qb;
+      window_total(payload(s.wa[q]), payload(s.wb[q]), kFan, lane, qa, qb);
+      pbb = __builtin_fmaf(qa, pbb, qb);
+      pba *= qa;
+    } else if (q == s.nw - 1) {  // the tile's own superblock, up to the tile
+      window_total(payload(s.wa[q]), payload(s.wb[q]), s.n0, lane, pf.p0a, pf.p0b);
     }
-    if (!rp) {
-      wpa = ld_status(&st.lvl0[ip].a);
-      wpb = ld_status(&st.lvl0[ip].b);
-      rp = word_ready(wpa, epoch) && word_ready(wpb, epoch);
-    }
-    if (!r1) {
-      w1a = ld_status(&st.lvl1[i1].a);
-      w1b = ld_status(&st.lvl1[i1].b);
-      r1 = word_ready(w1a, epoch) && word_ready(w1b, epoch);
-    }
-    if (!r2) {
-      w2a = ld_status(&st.lvl2[i2].a);
-      w2b = ld_status(&st.lvl2[i2].b);
-      r2 = word_ready(w2a, epoch) && word_ready(w2b, epoch);
-    }
-    const bool all0 = __ballot(!r0) == 0, allp = __ballot(!rp) == 0;
-    const bool all1 = __ballot(!r1) == 0, all2 = __ballot(!r2) == 0;
-    if (!pub1 && all0) {
-      float pa, pb;
-      window_total(payload(w0a), payload(w0b), n0, lane, pa, pb);
-      sbv = __builtin_fmaf(ga, pb, gb);  // (P0 (+) own aggregate)
-      sa = pa * ga;
-      if (lane == 0) {
-        st_status(&st.lvl1[sb].a, epoch, sa);
-        st_status(&st.lvl1[sb].b, epoch, sbv);
-      }
-      pub1 = true;
-    }
-    if (!pub2 && pub1 && all1 && allp) {
-      float p1a, p1b;
-      superblock_prefix(w1a, w1b, n1_old, wpa, wpb, use_prev, lane, p1a, p1b);
-      if (lane == 0) {
-        st_status(&st.lvl2[blk].a, epoch, p1a * sa);
-        st_status(&st.lvl2[blk].b, epoch, __builtin_fmaf(sa, p1b, sbv));
-      }
-      pub2 = true;
-    }
-    if (all0 && allp && all1 && all2 && pub1 && pub2) break;
-    __builtin_amdgcn_s_sleep(1);
   }
-  float p0a, p0b, p1a, p1b, p2a, p2b;
-  window_total(payload(w0a), payload(w0b), n0, lane, p0a, p0b);
-  superblock_prefix(w1a, w1b, n1_old, wpa, wpb, use_prev, lane, p1a, p1b);
-  window_total(payload(w2a), payload(w2b), n2, lane, p2a, p2b);
+  pf.pba = pba;
+  pf.pbb = pbb;
   const float h2 = __builtin_fmaf(p2a, h0, p2b);
-  const float h1 = __builtin_fmaf(p1a, h2, p1b);
-  return __builtin_fmaf(p0a, h1, p0b);
+  const float h1 = __builtin_fmaf(pba, h2, pbb);
+  pf.h_in = __builtin_fmaf(pf.p0a, h1, pf.p0b);
+  return pf;
+}
+
+// Once a tile's own aggregate (ga, gb) is known: the last tile of a
+// superblock publishes the superblock's aggregate (level 1), and the last tile
+// of a block the block's aggregate (level 2). For the last tile of a block,
+// blk1 is its own block, so PB (+) P0 (+) own covers the whole block.
+__device__ __forceinline__ void publish_higher(const LinearStatus &st, int64_t tile,
+                                               const Prefix &pf, float ga, float gb,
+                                               uint32_t epoch, int lane) {
+  const int64_t sb = tile / kFan;
+  const int64_t blk = sb / kFan;
+  if (tile - sb * kFan != kFan - 1 || lane != 0) return;
+  const float sbb = __builtin_fmaf(ga, pf.p0b, gb);  // P0 (+) own aggregate
+  const float sba = pf.p0a * ga;
+  st_status(&st.lvl1[sb].a, epoch, sba);
+  st_status(&st.lvl1[sb].b, epoch, sbb);
+  if (sb - blk * kFan == kFan - 1) {
+    st_status(&st.lvl2[blk].a, epoch, pf.pba * sba);
+    st_status(&st.lvl2[blk].b, epoch, __builtin_fmaf(sba, pf.pbb, sbb));
+  }
 }
 
 // Loads one tile (rows of float4 per wave); past n the identity map (1, 0).
@@ -347,51 +378,78 @@ __device__ __forceinline__ int64_t claim_batch(unsigned long long *ticket, int l
 __device__ __forceinline__ int64_t successor(int64_t t, int64_t ntiles,
                                              unsigned long long *ticket, int lane) {
   if (t >= ntiles) return ntiles;
+  if (t < 0) {  // nothing claimed yet
+    const int64_t first = claim_batch(ticket, lane) * kClaimTiles;
+    return first < ntiles ? first : ntiles;
+  }
   if ((t + 1) % kClaimTiles != 0) return t + 1 < ntiles ? t + 1 : ntiles;
   const int64_t first = claim_batch(ticket, lane) * kClaimTiles;
   return first < ntiles ? first : ntiles;
 }
 
-// LDS shared by the waves of one workgroup. Everything one iteration hands
-// across a barrier is double-buffered by iteration parity: a wave may run one
-// iteration ahead of another between two barriers, and must not overwrite a
-// value the other still has to read.
+// LDS shared by the waves of one workgroup. Per-tile values are kept in
+// 4-entry rings indexed by the tile's position j in the workgroup's sequence
+// (j % 4): a tile's entries are written two iterations before the last read,
+// and every hand-over crosses a barrier. The parked a/b of two tiles wait
+// there for their look-backs (slot j % 2; each wave reads back only what it
+// wrote itself).
 struct Shared {
-  float wave_a[2][kWaves], wave_b[2][kWaves];  // per-wave aggregates
-  float tile_a[2], tile_b[2];                  // tile aggregates
-  float carry[2][kWaves];                      // h entering each wave's rows
-  int64_t first[2];                            // first two claimed tiles
-  int64_t after[2];                            // tile claimed for the iteration after next
+  float4 park[2][kWaves][kRows][2][64];        // a, b rows of two parked tiles
+  float wave_a[4][kWaves], wave_b[4][kWaves];  // per-wave aggregates
+  float tile_a[4], tile_b[4];                  // tile aggregates
+  float carry[4][kWaves];                      // h entering each wave's rows
+  int64_t ids[4];                              // claimed tiles, in claim order
   unsigned arrived[2];                         // data waves done with a tile's local scan
 };
+
+__device__ __forceinline__ void park(Shared &sh, int slot, const float4 (&va)[kRows],
+                                     const float4 (&vb)[kRows]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    sh.park[slot][wave][r][0][lane] = va[r];
+    sh.park[slot][wave][r][1][lane] = vb[r];
+  }
+}
+__device__ __forceinline__ void unpark(const Shared &sh, int slot, float4 (&va)[kRows],
+                                       float4 (&vb)[kRows]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    va[r] = sh.park[slot][wave][r][0][lane];
+    vb[r] = sh.park[slot][wave][r][1][lane];
+  }
+}
 
 // Data waves: local scan of a loaded tile; the last data wave to finish folds
 // the wave aggregates into the tile aggregate and publishes it (level 0) at
 // once, without waiting for any other workgroup.
 __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
                                                  const float4 (&vb)[kRows], float (&ia)[kRows],
-                                                 float (&ib)[kRows], Shared &sh, int slot,
+                                                 float (&ib)[kRows], Shared &sh, int ring, int slot,
                                                  const LinearStatus &st, int64_t tile,
                                                  uint32_t epoch) {
   const int lane = threadIdx.x & 63;
-  tile_local_scan(va, vb, ia, ib, sh.wave_a[slot], sh.wave_b[slot]);
+  tile_local_scan(va, vb, ia, ib, sh.wave_a[ring], sh.wave_b[ring]);
   unsigned prior = 0;
   if (lane == 0)
     prior = __hip_atomic_fetch_add(&sh.arrived[slot], 1u, __ATOMIC_ACQ_REL,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
   prior = __builtin_amdgcn_readfirstlane(prior);
   if (prior == kWaves - 1) {
-    float ga = sh.wave_a[slot][0], gb = sh.wave_b[slot][0];
+    float ga = sh.wave_a[ring][0], gb = sh.wave_b[ring][0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      gb = __builtin_fmaf(sh.wave_a[slot][w], gb, sh.wave_b[slot][w]);
-      ga *= sh.wave_a[slot][w];
+      gb = __builtin_fmaf(sh.wave_a[ring][w], gb, sh.wave_b[ring][w]);
+      ga *= sh.wave_a[ring][w];
     }
     if (lane == 0) {
       st_status(&st.lvl0[tile].a, epoch, ga);
       st_status(&st.lvl0[tile].b, epoch, gb);
-      sh.tile_a[slot] = ga;
-      sh.tile_b[slot] = gb;
+      sh.tile_a[ring] = ga;
+      sh.tile_b[ring] = gb;
       sh.arrived[slot] = 0;  // reused two tiles later, after two barriers
     }
   }
@@ -405,19 +463,28 @@ __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
 // chains the batches' last tiles one after another (measured: 2 tiles per
 // ticket 1.75x slower, 4 tiles per ticket fully serialised).
 //
-// Within a workgroup, four data waves and one control wave overlap two tiles:
-// while the control wave runs the look-back of tile c_i (whose aggregate was
-// published one iteration earlier), the data waves load tile c_{i+1}, claim
-// c_{i+2}, scan c_{i+1} and publish its aggregate; then the data waves apply
-// c_i's carries and store it. Publishing a tile therefore never waits for its own workgroup's
-// previous look-back to finish, which would chain every tile's publication to
-// the look-back of an earlier tile. The control wave issues no data loads, so
-// its status reads never queue behind outstanding data loads (the vector
-// memory counter retires in order).
+// A workgroup's tiles t_0, t_1, ... move through a pipeline, one stage per
+// iteration; in iteration j, between barriers C_{j-1} and C_j:
+//   data waves   - issue the loads of t_{j+2} (wave 0 first claims t_{j+3}),
+//                  scan t_{j+1} (loaded one iteration earlier) and publish its
+//                  level-0 aggregate; after C_j, apply t_{j-1}'s carries to
+//                  its parked a/b, store it, and park t_{j+1}'s a/b in the
+//                  slot t_{j-1} left;
+//   control wave - issues the first status reads of t_j's look-back together
+//                  with the next reads of t_{j-1}'s, finishes t_{j-1}'s
+//                  look-back, publishes its higher-level aggregates if it is
+//                  the last tile of a superblock or block, and leaves the
+//                  carries of its waves in LDS.
+// So a tile's loads have an iteration to arrive, its look-back starts an
+// iteration after its predecessors were published and has an iteration and
+// a half to finish, and the control wave's status reads never queue behind
+// data loads (the vector memory counter retires in order). The claim atomic
+// is issued ahead of the loads it must not wait for, and its result is read
+// one barrier later.
 //
 // Every wait is for something a lower tile produces before it waits on
 // anything itself (level-0 aggregates right after its local scan, higher
-// levels from the look-back of a lower tile), and a workgroup only waits on
+// levels after the look-back of a lower tile), and a workgroup only waits on
 // tiles lower than the ones it owns; so the lowest unfinished tile can always
 // finish, however many workgroups the device keeps resident.
 // The ticket of a launch is st.ticket[epoch & 1]; the first workgroup zeroes
@@ -434,70 +501,105 @@ __global__ __launch_bounds__(kThreads + 64) void linear_scan_kernel(
     if (blockIdx.x == 0 && lane == 0)
       __hip_atomic_store(st.ticket + ((epoch + 1u) & 1u), 0ull, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-    int64_t cur = claim_batch(ticket, lane) * kClaimTiles;
-    if (cur > ntiles) cur = ntiles;
-    int64_t nxt = successor(cur, ntiles, ticket, lane);
+    const int64_t t0 = successor(-1, ntiles, ticket, lane);
+    const int64_t t1 = successor(t0, ntiles, ticket, lane);
+    const int64_t t2 = successor(t1, ntiles, ticket, lane);
     if (lane == 0) {
-      sh.first[0] = cur;
-      sh.first[1] = nxt;
+      sh.ids[0] = t0;
+      sh.ids[1] = t1;
+      sh.ids[2] = t2;
       sh.arrived[0] = 0;
       sh.arrived[1] = 0;
     }
     __syncthreads();  // A: first claims visible
-    __syncthreads();  // B: first tile scanned and published
-    for (int slot = 0; cur < ntiles; slot ^= 1) {
-      const float ga = sh.tile_a[slot], gb = sh.tile_b[slot];
-      const float h_in = look_back(st, cur, ga, gb, h0, epoch, lane);
-      if (lane == 0) {
-        float c = h_in;
-        for (int w = 0; w < kWaves; ++w) {
-          sh.carry[slot][w] = c;
-          c = __builtin_fmaf(sh.wave_a[slot][w], c, sh.wave_b[slot][w]);
+    __syncthreads();  // B: t_0 scanned and published
+    // Look-backs of t_{j-1} (lp) and t_j (ln). t_j's first status reads are
+    // issued at the end of iteration j and read at the start of iteration j+1,
+    // so their round trip overlaps the barrier and the data waves' work. The
+    // two LookBack variables swap roles every iteration (the loop is unrolled
+    // by two) rather than being copied, since a copy would wait for the reads.
+    LookBack l0, l1;
+    int64_t tp = ntiles;
+    int j = 0;
+    auto step = [&](LookBack &lp, LookBack &ln) {
+      const int64_t tn = sh.ids[j & 3];  // claimed before barrier C of iteration j-3
+      if (tp < ntiles) {
+        lb_check(lp, epoch);
+        while (!lb_done(lp)) {
+          __builtin_amdgcn_s_sleep(1);
+          lb_issue(lp, st, lane);
+          lb_check(lp, epoch);
+        }
+        const int rp = (j - 1) & 3;
+        const Prefix pf = lb_finish(lp, h0, lane);
+        publish_higher(st, tp, pf, sh.tile_a[rp], sh.tile_b[rp], epoch, lane);
+        if (lane == 0) {
+          float c = pf.h_in;
+          for (int w = 0; w < kWaves; ++w) {
+            sh.carry[rp][w] = c;
+            c = __builtin_fmaf(sh.wave_a[rp][w], c, sh.wave_b[rp][w]);
+          }
         }
       }
-      __syncthreads();  // C: carries of `cur`, tile after `nxt`, `nxt` published
-      cur = nxt;
-      nxt = sh.after[slot];
+      if (tn < ntiles) {
+        lb_init(ln, tn, lane);
+        lb_issue(ln, st, lane);
+      }
+      tp = tn;
+      __syncthreads();  // C_j: carries of t_{j-1}; t_{j+1} published; t_{j+3} claimed
+      ++j;
+    };
+    for (;;) {
+      step(l0, l1);
+      if (tp >= ntiles) break;
+      step(l1, l0);
+      if (tp >= ntiles) break;
     }
     return;
   }
 
   __syncthreads();  // A
-  int64_t cur = sh.first[0], nxt = sh.first[1];
-  float4 va[kRows], vb[kRows];
-  float ia[kRows], ib[kRows];
-  if (cur < ntiles) {
-    load_tile(a, b, n, cur, va, vb);
-    scan_and_publish(va, vb, ia, ib, sh, 0, st, cur, epoch);
+  int64_t tp = ntiles, t0 = sh.ids[0], t1 = sh.ids[1], t2 = sh.ids[2];
+  // Register stages: (va, vb) tile being applied, (na, nb) tile being
+  // scanned, (ma, mb) tile being loaded; prefixes of the two parked tiles.
+  float4 va[kRows], vb[kRows], na[kRows], nb[kRows];
+  float iap[kRows], ibp[kRows], iaw[kRows], ibw[kRows];
+  if (t0 < ntiles) load_tile(a, b, n, t0, va, vb);
+  if (t1 < ntiles) load_tile(a, b, n, t1, na, nb);
+  if (t0 < ntiles) {
+    scan_and_publish(va, vb, iaw, ibw, sh, 0, 0, st, t0, epoch);
+    park(sh, 0, va, vb);
   }
   __syncthreads();  // B
-  for (int slot = 0; cur < ntiles; slot ^= 1) {
-    float4 na[kRows], nb[kRows];
+  // In iteration j: tp = t_{j-1}, t0 = t_j, t1 = t_{j+1}, t2 = t_{j+2}.
+  for (int j = 0; j == 0 || tp < ntiles; ++j) {
+    int64_t claimed = ntiles;
+    if (wave == 0 && t2 < ntiles) claimed = successor(t2, ntiles, ticket, lane);
+    float4 ma[kRows], mb[kRows];
+    if (t2 < ntiles) load_tile(a, b, n, t2, ma, mb);
     float nia[kRows], nib[kRows];
-    if (nxt < ntiles) {
-      load_tile(a, b, n, nxt, na, nb);
-      // Wave 0 finds (claiming if needed) the tile after `nxt`; a claim's
-      // latency overlaps the loads it was queued behind, not the look-back.
-      if (wave == 0) {
-        const int64_t after = successor(nxt, ntiles, ticket, lane);
-        if (lane == 0) sh.after[slot] = after;
-      }
-      scan_and_publish(na, nb, nia, nib, sh, slot ^ 1, st, nxt, epoch);
-    } else if (wave == 0 && lane == 0) {
-      sh.after[slot] = ntiles;
+    if (t1 < ntiles)
+      scan_and_publish(na, nb, nia, nib, sh, (j + 1) & 3, (j + 1) & 1, st, t1, epoch);
+    if (wave == 0 && lane == 0) sh.ids[(j + 3) & 3] = claimed;
+    __syncthreads();  // C_j
+    if (tp < ntiles) {
+      unpark(sh, (j + 1) & 1, va, vb);  // t_{j-1} sits in slot (j - 1) % 2
+      tile_apply(va, vb, iap, ibp, sh.carry[(j - 1) & 3][wave], h, n, tp);
     }
-    __syncthreads();  // C
-    tile_apply(va, vb, ia, ib, sh.carry[slot][wave], h, n, cur);
-    const int64_t after = sh.after[slot];
+    if (t1 < ntiles) park(sh, (j + 1) & 1, na, nb);
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      va[r] = na[r];
-      vb[r] = nb[r];
-      ia[r] = nia[r];
-      ib[r] = nib[r];
+      iap[r] = iaw[r];
+      ibp[r] = ibw[r];
+      iaw[r] = nia[r];
+      ibw[r] = nib[r];
+      na[r] = ma[r];
+      nb[r] = mb[r];
     }
-    cur = nxt;
-    nxt = after;
+    tp = t0;
+    t0 = t1;
+    t1 = t2;
+    t2 = sh.ids[(j + 3) & 3];
   }
 }
 
