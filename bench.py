@@ -194,6 +194,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-s6", action="store_true")
+    ap.add_argument("--s6-only", choices=S6_BENCH,
+                    help="time only this S6 workload (for per-workload profiles) and print its record")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--exp-cost", type=float, default=2.0,
                     help="lane-cycles one v_exp_f32 occupies relative to an FMA")
@@ -212,6 +214,10 @@ def main():
     if not sentinel_ok(dev):
         raise SystemExit("sentinel copy kernel did not reproduce its input; sweep discarded")
 
+    if args.s6_only:
+        print(json.dumps(bench_s6(dev, args.s6_only, args.steps, args.warmup, args.exp_cost)),
+              flush=True)
+        return
     copy_gbs = bench_copy(dev, 10, 3)
     log(f"copy kernel: {copy_gbs:.0f} GB/s")
     n, ms_step, ms_kernel, ms_min = bench_linear(dev, args.steps, args.warmup)

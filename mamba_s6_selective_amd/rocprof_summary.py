@@ -3,6 +3,9 @@
     python -m mamba_s6_selective_amd.rocprof_summary stats RUN_results.db ...
         per-kernel call count and average / total duration (kernel trace)
 
+    python -m mamba_s6_selective_amd.rocprof_summary counters RUN_results.db
+        per-kernel median over dispatches of every counter the run collected
+
     python -m mamba_s6_selective_amd.rocprof_summary traffic \\
         --fetch FETCH_results.db --write WRITE_results.db \\
         --kernel linear_scan_kernel --copy-bytes 1073741824 --source linear_scan.hip \\
@@ -69,6 +72,18 @@ def cmd_stats(args):
             print(f"{name[:60]:<60} {calls:>6} {avg:>10.2f} {total:>12.1f}")
 
 
+def cmd_counters(args):
+    con = sqlite3.connect(args.db)
+    names = sorted({r[0] for r in con.execute(
+        "select distinct counter_name from counters_collection")})
+    per = {c: counter_per_dispatch(args.db, c) for c in names}
+    kernels = sorted({k for d in per.values() for k in d})
+    print(f"{'kernel':<48} " + " ".join(f"{c:>24}" for c in names))
+    for k in kernels:
+        vals = [statistics.median(per[c][k]) if per[c].get(k) else float("nan") for c in names]
+        print(f"{k[:48]:<48} " + " ".join(f"{v:>24.4g}" for v in vals))
+
+
 def pick(d, key):
     hits = [k for k in d if key in k]
     if not hits:
@@ -106,6 +121,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dbs", nargs="+")
+    c = sub.add_parser("counters")
+    c.add_argument("db")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -114,7 +131,7 @@ def main(argv=None):
     t.add_argument("--source", required=True)
     t.add_argument("--out")
     args = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[args.cmd](args)
+    {"stats": cmd_stats, "counters": cmd_counters, "traffic": cmd_traffic}[args.cmd](args)
 
 
 if __name__ == "__main__":
