@@ -97,6 +97,27 @@ def bench_linear(dev, steps, warmup):
     return n, ms_step, ms_kernel, ms_min
 
 
+def bench_linear_3pass(dev, steps, warmup, ms_single):
+    """The three-pass design on the same workload, for the pages' traffic model:
+    28 B/element (read a, b; write and re-read the in-tile compositions A, B;
+    write h) against the single pass's 12, so a predicted ratio of 28/12."""
+    import torch
+    import mamba_s6_selective_amd as ssm
+    from mamba_s6_selective_amd.workloads import LINEAR_WORKLOADS, linear_workload_inputs
+    n = LINEAR_WORKLOADS[LINEAR_WORKLOAD]["n"]
+    a, b = linear_workload_inputs(LINEAR_WORKLOAD)
+    a, b = a.to(dev), b.to(dev)
+    h = torch.empty_like(a)
+    _, ms_kernel, _ = time_steps(lambda: ssm.linear_scan_3pass(a, b, 0.0, out=h), steps, warmup)
+    return {
+        "workload": LINEAR_WORKLOAD, "ms_per_launch": round(ms_kernel, 4),
+        "bytes_per_elem": 28, "single_pass_bytes_per_elem": LINEAR_BYTES_PER_ELEM,
+        "achieved_GBs": round(28 * n / (ms_kernel * 1e-3) / 1e9, 1),
+        "predicted_ratio": round(28 / LINEAR_BYTES_PER_ELEM, 3),
+        "measured_ratio": round(ms_kernel / ms_single, 3),
+    }
+
+
 def bench_copy(dev, steps, warmup):
     import torch
     import mamba_s6_selective_amd as ssm
@@ -241,6 +262,9 @@ def main():
                      "traffic": traffic},
         "copy_kernel_GBs": round(copy_gbs, 1),
     }
+    record["three_pass"] = bench_linear_3pass(dev, max(5, args.steps // 2), 2, ms_kernel)
+    log(f"three-pass: {record['three_pass']['ms_per_launch'] * 1e3:.1f} us, ratio "
+        f"{record['three_pass']['measured_ratio']} (model {record['three_pass']['predicted_ratio']})")
     if not args.no_s6:
         record["s6"] = [bench_s6(dev, name, max(5, args.steps // 2), 2, args.exp_cost)
                         for name in S6_BENCH]

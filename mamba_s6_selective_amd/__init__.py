@@ -24,6 +24,7 @@ SSM_ERR_ALLOC = -4
 _P = ctypes.c_void_p
 SIGNATURES = {
     "ssm_linear_scan": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
+    "ssm_linear_scan_3pass": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
     "ssm_selective_scan_fwd": (ctypes.c_int, [_P] * 7 + [ctypes.c_int] * 5 + [_P]),
     "ssm_selective_scan_fwd_bf16": (ctypes.c_int, [_P] * 7 + [ctypes.c_int] * 5 + [_P]),
     "ssm_copy_f32": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
@@ -81,6 +82,32 @@ def _dev_tensor(t, name, dtypes):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _linear_args(a, b, out):
+    import torch
+    _dev_tensor(a, "a", (torch.float32,))
+    _dev_tensor(b, "b", (torch.float32,))
+    if a.shape != b.shape or a.dim() != 1:
+        raise ValueError("a and b must be 1-D and of equal length")
+    if out is None:
+        out = torch.empty_like(a)
+    else:
+        _dev_tensor(out, "out", (torch.float32,))
+        if out.shape != a.shape:
+            raise ValueError("out must match a")
+    return out
+
+
+def linear_scan_3pass(a, b, h0: float = 0.0, out=None):
+    """The same recurrence by the three-pass design (28 B/element of traffic)."""
+    import torch
+    lib = load_library()
+    out = _linear_args(a, b, out)
+    with torch.cuda.device(a.device):
+        _check(lib.ssm_linear_scan_3pass(a.data_ptr(), b.data_ptr(), float(h0),
+                                         out.data_ptr(), a.numel(), _stream(a)))
+    return out
 
 
 def linear_scan(a, b, h0: float = 0.0, out=None):

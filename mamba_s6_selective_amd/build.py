@@ -12,7 +12,7 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libssmscan.so"
-SOURCES = ["ssmscan.cpp", "linear_scan.hip", "s6_scan.hip"]
+SOURCES = ["ssmscan.cpp", "linear_scan.hip", "linear_3pass.hip", "s6_scan.hip"]
 
 # Packed-FP32 instructions are switched off for every HIP source; the
 # compiler otherwise forms them on its own from scalar float code.

@@ -54,4 +54,14 @@ int linear_wgs_per_cu();
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n,
                            hipStream_t stream);
 
+// ---- three-pass linear recurrence ------------------------------------------
+
+int64_t linear3_tile_elems();
+// Device workspace the three-pass scan needs for n elements.
+size_t linear3_workspace_bytes(int64_t n);
+// Enqueues the local, carry and apply passes; `workspace` holds at least
+// linear3_workspace_bytes(n) bytes, 256-byte aligned.
+hipError_t launch_linear_scan_3pass(const float *a, const float *b, float h0, float *h,
+                                    int64_t n, void *workspace, hipStream_t stream);
+
 }  // namespace ssm

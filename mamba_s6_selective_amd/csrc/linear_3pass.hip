@@ -1,0 +1,221 @@
+// Three-pass scan of the affine recurrence h[t] = a[t]*h[t-1] + b[t],
+// h[-1] = h0 ("Selective-scan CUDA kernels": the three-pass multi-block
+// version that the page's memory-traffic model compares the single-pass
+// look-back against).
+//
+//  1. local pass: each tile of 8192 elements composes its maps in order and
+//     writes, for every element, the composition (A, B) of the tile's maps up
+//     to and including it (8 B read, 8 B written per element), plus the
+//     tile's aggregate;
+//  2. carry pass: one workgroup folds the tile aggregates left to right and
+//     writes the value of h entering every tile;
+//  3. apply pass: h = A * h_in(tile) + B (8 B read, 4 B written per element).
+//
+// 28 B of HBM traffic per element against the single pass's 12 (read a, b;
+// write h): the traffic model predicts the single pass 28/12 = 2.33x faster
+// when both run at the same fraction of the bandwidth. The passes use the same
+// composition rule and fixed shapes, so the result is deterministic.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "scan_common.h"
+
+namespace ssm {
+namespace {
+
+using namespace scan;
+
+constexpr int kWaves = 4;
+constexpr int kRows = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowElems = 256;                   // 64 lanes x float4
+constexpr int kWaveElems = kRowElems * kRows;    // 2048
+constexpr int kTileElems = kWaveElems * kWaves;  // 8192
+
+// Composition (x (+) y), x earlier.
+__device__ __forceinline__ void compose(float xa, float xb, float ya, float yb, float &ra,
+                                        float &rb) {
+  rb = __builtin_fmaf(ya, xb, yb);
+  ra = xa * ya;
+}
+
+__global__ __launch_bounds__(kThreads) void local_kernel(const float *__restrict__ a,
+                                                         const float *__restrict__ b,
+                                                         float *__restrict__ pa,
+                                                         float *__restrict__ pb,
+                                                         float *__restrict__ agg, int64_t n) {
+  __shared__ float s_wa[kWaves], s_wb[kWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t tile = blockIdx.x;
+  const int64_t wave_start = tile * kTileElems + int64_t(wave) * kWaveElems;
+  const bool full = (tile + 1) * kTileElems <= n;
+  float4 va[kRows], vb[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int64_t off = wave_start + r * kRowElems + lane * 4;
+    if (full) {
+      va[r] = load_nt(a + off);
+      vb[r] = load_nt(b + off);
+    } else {  // past n: the identity map (1, 0)
+      float ta[4], tb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = off + j < n;
+        ta[j] = in ? a[off + j] : 1.0f;
+        tb[j] = in ? b[off + j] : 0.0f;
+      }
+      va[r] = make_float4(ta[0], ta[1], ta[2], ta[3]);
+      vb[r] = make_float4(tb[0], tb[1], tb[2], tb[3]);
+    }
+  }
+  // Per row: the lanes' exclusive prefixes within the row; the rows' prefixes
+  // within the wave (serial); the wave's total.
+  float ea[kRows], eb[kRows];
+  float ra = 1.0f, rb = 0.0f;  // composition of the wave's earlier rows
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    float ca = va[r].x, cb = vb[r].x;
+    compose(ca, cb, va[r].y, vb[r].y, ca, cb);
+    compose(ca, cb, va[r].z, vb[r].z, ca, cb);
+    compose(ca, cb, va[r].w, vb[r].w, ca, cb);
+    wave_scan(ca, cb);
+    const float xa = dpp<kWaveShr1, 0xf, 0xf>(1.0f, ca);  // lanes before this one
+    const float xb = dpp<kWaveShr1, 0xf, 0xf>(0.0f, cb);
+    compose(ra, rb, xa, xb, ea[r], eb[r]);
+    compose(ra, rb, lane_f(ca, 63), lane_f(cb, 63), ra, rb);
+  }
+  if (lane == 0) {
+    s_wa[wave] = ra;
+    s_wb[wave] = rb;
+  }
+  __syncthreads();
+  float wa = 1.0f, wb = 0.0f;  // composition of the tile's earlier waves
+  for (int w = 0; w < wave; ++w) compose(wa, wb, s_wa[w], s_wb[w], wa, wb);
+  if (wave == kWaves - 1 && lane == 0) {
+    float ta, tb;
+    compose(wa, wb, ra, rb, ta, tb);
+    agg[2 * tile] = ta;
+    agg[2 * tile + 1] = tb;
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    float qa, qb;
+    compose(wa, wb, ea[r], eb[r], qa, qb);  // everything before the lane's first item
+    float4 oa, ob;
+    compose(qa, qb, va[r].x, vb[r].x, oa.x, ob.x);
+    compose(oa.x, ob.x, va[r].y, vb[r].y, oa.y, ob.y);
+    compose(oa.y, ob.y, va[r].z, vb[r].z, oa.z, ob.z);
+    compose(oa.z, ob.z, va[r].w, vb[r].w, oa.w, ob.w);
+    const int64_t off = wave_start + r * kRowElems + lane * 4;
+    if (full) {
+      store_nt(pa + off, oa);
+      store_nt(pb + off, ob);
+    } else {
+      const float xa4[4] = {oa.x, oa.y, oa.z, oa.w}, xb4[4] = {ob.x, ob.y, ob.z, ob.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (off + j < n) {
+          pa[off + j] = xa4[j];
+          pb[off + j] = xb4[j];
+        }
+    }
+  }
+}
+
+// One workgroup: thread i folds tiles [i*per, (i+1)*per), the threads'
+// totals are scanned (wave DPP scans, then the waves' totals in LDS), and each
+// thread re-walks its tiles writing the value of h entering each.
+constexpr int kCarryThreads = 1024;
+
+__global__ __launch_bounds__(kCarryThreads) void carry_kernel(const float *__restrict__ agg,
+                                                              float *__restrict__ hin,
+                                                              float h0, int64_t ntiles,
+                                                              int64_t per) {
+  __shared__ float s_a[kCarryThreads / 64], s_b[kCarryThreads / 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t0 = int64_t(threadIdx.x) * per;
+  float ta = 1.0f, tb = 0.0f;
+  for (int64_t k = 0; k < per; ++k) {
+    const int64_t t = t0 + k;
+    if (t < ntiles) compose(ta, tb, agg[2 * t], agg[2 * t + 1], ta, tb);
+  }
+  float ia = ta, ib = tb;
+  wave_scan(ia, ib);
+  if (lane == 63) {
+    s_a[wave] = ia;
+    s_b[wave] = ib;
+  }
+  __syncthreads();
+  float wa = 1.0f, wb = 0.0f;  // earlier waves
+  for (int w = 0; w < wave; ++w) compose(wa, wb, s_a[w], s_b[w], wa, wb);
+  const float xa = dpp<kWaveShr1, 0xf, 0xf>(1.0f, ia);  // earlier lanes of this wave
+  const float xb = dpp<kWaveShr1, 0xf, 0xf>(0.0f, ib);
+  float pa, pb;
+  compose(wa, wb, xa, xb, pa, pb);
+  float h = __builtin_fmaf(pa, h0, pb);
+  for (int64_t k = 0; k < per; ++k) {
+    const int64_t t = t0 + k;
+    if (t < ntiles) {
+      hin[t] = h;
+      h = __builtin_fmaf(agg[2 * t], h, agg[2 * t + 1]);
+    }
+  }
+}
+
+// 1024 elements per workgroup (one float4 per thread); the tile's incoming
+// value is wave-uniform.
+__global__ __launch_bounds__(256) void apply_kernel(const float *__restrict__ pa,
+                                                    const float *__restrict__ pb,
+                                                    const float *__restrict__ hin,
+                                                    float *__restrict__ h, int64_t n) {
+  const int64_t off = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const float c = hin[(int64_t(blockIdx.x) * 1024) / kTileElems];
+  if (off + 4 <= n) {
+    const float4 A = load_nt(pa + off), B = load_nt(pb + off);
+    float4 o;
+    o.x = __builtin_fmaf(A.x, c, B.x);
+    o.y = __builtin_fmaf(A.y, c, B.y);
+    o.z = __builtin_fmaf(A.z, c, B.z);
+    o.w = __builtin_fmaf(A.w, c, B.w);
+    store_nt(h + off, o);
+  } else {
+    for (int64_t i = off; i < n; ++i) h[i] = __builtin_fmaf(pa[i], c, pb[i]);
+  }
+}
+
+}  // namespace
+
+int64_t linear3_tile_elems() { return kTileElems; }
+
+size_t linear3_workspace_bytes(int64_t n) {
+  const int64_t ntiles = (n + kTileElems - 1) / kTileElems;
+  const auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  return up(size_t(n) * 4) * 2 + up(size_t(ntiles) * 8) + up(size_t(ntiles) * 4);
+}
+
+hipError_t launch_linear_scan_3pass(const float *a, const float *b, float h0, float *h,
+                                    int64_t n, void *workspace, hipStream_t stream) {
+  const int64_t ntiles = (n + kTileElems - 1) / kTileElems;
+  const auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  char *w = static_cast<char *>(workspace);
+  float *pa = reinterpret_cast<float *>(w);
+  float *pb = reinterpret_cast<float *>(w + up(size_t(n) * 4));
+  float *agg = reinterpret_cast<float *>(w + 2 * up(size_t(n) * 4));
+  float *hin = reinterpret_cast<float *>(w + 2 * up(size_t(n) * 4) + up(size_t(ntiles) * 8));
+  hipLaunchKernelGGL(local_kernel, dim3(unsigned(ntiles)), dim3(kThreads), 0, stream, a, b, pa,
+                     pb, agg, n);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const int64_t per = (ntiles + kCarryThreads - 1) / kCarryThreads;
+  hipLaunchKernelGGL(carry_kernel, dim3(1), dim3(kCarryThreads), 0, stream, agg, hin, h0, ntiles,
+                     per);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const int64_t groups = (n + 1023) / 1024;
+  hipLaunchKernelGGL(apply_kernel, dim3(unsigned(groups)), dim3(256), 0, stream, pa, pb, hin, h,
+                     n);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -50,6 +50,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "scan_common.h"
 
 namespace ssm {
 namespace {
@@ -62,41 +63,7 @@ constexpr int kWaveElems = kRowElems * kRows;     // 1024
 constexpr int kTileElems = kWaveElems * kWaves;   // 8192
 constexpr int kFan = 64;                          // entries per look-back window
 
-// DPP controls (GFX9 encoding).
-constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
-
-template <int Ctrl, int RowMask, int BankMask>
-__device__ __forceinline__ float dpp(float old, float src) {
-  // Lanes whose source is out of the row/wave, or that are masked off, keep `old`.
-  return __int_as_float(__builtin_amdgcn_update_dpp(
-      __float_as_int(old), __float_as_int(src), Ctrl, RowMask, BankMask, false));
-}
-
-// One Hillis-Steele step: (a, b) <- (a', b') (+) (a, b) where (a', b') comes
-// from the lane the DPP control selects; lanes with no such lane combine with
-// the identity (1, 0).
-template <int Ctrl, int RowMask, int BankMask>
-__device__ __forceinline__ void scan_step(float &a, float &b) {
-  const float pa = dpp<Ctrl, RowMask, BankMask>(1.0f, a);
-  const float pb = dpp<Ctrl, RowMask, BankMask>(0.0f, b);
-  b = __builtin_fmaf(a, pb, b);
-  a = pa * a;
-}
-
-// Inclusive wave64 scan of affine pairs in lane order (lane 0 earliest).
-__device__ __forceinline__ void wave_scan(float &a, float &b) {
-  scan_step<kRowShr1, 0xf, 0xf>(a, b);
-  scan_step<kRowShr2, 0xf, 0xf>(a, b);
-  scan_step<kRowShr4, 0xf, 0xf>(a, b);
-  scan_step<kRowShr8, 0xf, 0xf>(a, b);
-  scan_step<kRowBcast15, 0xa, 0xf>(a, b);   // rows 1, 3 take row 0, 2 totals
-  scan_step<kRowBcast31, 0xc, 0xf>(a, b);   // rows 2, 3 take rows 0-1 total
-}
-
-__device__ __forceinline__ float lane_f(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
+using namespace scan;
 
 __device__ __forceinline__ uint64_t ld_status(const uint64_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -107,18 +74,6 @@ __device__ __forceinline__ void st_status(uint64_t *p, uint32_t epoch, float v) 
 }
 __device__ __forceinline__ float payload(uint64_t w) {
   return __uint_as_float(uint32_t(w));
-}
-
-// Streaming (non-temporal) 16-byte loads and stores: a, b and h are touched
-// exactly once, so they should not displace anything in L2 or the MALL.
-typedef float v4f __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 load_nt(const float *p) {
-  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p));
-  return make_float4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void store_nt(float *p, float4 o) {
-  const v4f v = {o.x, o.y, o.z, o.w};
-  __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(p));
 }
 
 __device__ __forceinline__ bool word_ready(uint64_t w, uint32_t epoch) {

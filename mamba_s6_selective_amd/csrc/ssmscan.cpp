@@ -37,10 +37,17 @@ struct S6Workspace {
   uint32_t epoch = 0;
 };
 
+// Plain scratch memory for one (device, stream), grown on demand.
+struct ScratchWorkspace {
+  void *buf = nullptr;
+  size_t bytes = 0;
+};
+
 using Key = std::pair<int, hipStream_t>;
 std::mutex g_mu;
 std::map<Key, LinearWorkspace> g_linear;
 std::map<Key, S6Workspace> g_s6;
+std::map<Key, ScratchWorkspace> g_scratch;
 std::map<int, int> g_linear_grid;  // device -> resident workgroups of the scan kernel
 
 int current_device(int *dev) {
@@ -166,6 +173,33 @@ int s6_workspace(hipStream_t stream, size_t bytes, int64_t tickets, void **buf,
   return SSM_OK;
 }
 
+// Cached scratch buffer for (current device, stream), at least `bytes` long
+// and 256-byte aligned. Growing it waits for the stream, whose queued work
+// may still use the old buffer.
+static int scratch_workspace(hipStream_t stream, size_t bytes, void **buf) {
+  int dev = 0;
+  if (int rc = current_device(&dev)) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  ScratchWorkspace &ws = g_scratch[Key(dev, stream)];
+  if (ws.bytes < bytes || ws.buf == nullptr) {
+    if (ws.buf) {
+      if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
+      (void)hipFree(ws.buf);
+      ws.buf = nullptr;
+      ws.bytes = 0;
+    }
+    size_t cap = 1 << 20;
+    while (cap < bytes) cap *= 2;
+    void *p = nullptr;
+    if (hipMalloc(&p, cap) != hipSuccess)
+      return fail(SSM_ERR_ALLOC, "hipMalloc of the scratch workspace failed");
+    ws.buf = p;
+    ws.bytes = cap;
+  }
+  *buf = ws.buf;
+  return SSM_OK;
+}
+
 }  // namespace ssm
 
 using namespace ssm;
@@ -191,6 +225,21 @@ int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t 
   if (int rc = linear_workspace(s, ntiles, &status, &epoch, &grid)) return rc;
   return hip_check(launch_linear_scan(a, b, h0, h, n, ntiles, status, epoch, grid, s),
                    "linear_scan launch");
+}
+
+int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, int64_t n,
+                          void *stream) {
+  g_last_error.clear();
+  if (n < 0) return fail(SSM_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return SSM_OK;
+  if (!a || !b || !h) return fail(SSM_ERR_INVALID_ARG, "null pointer with n > 0");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(h))
+    return fail(SSM_ERR_INVALID_ARG, "a, b and h must be 16-byte aligned");
+  if (n > (int64_t(1) << 31)) return fail(SSM_ERR_UNSUPPORTED, "n too large (max 2^31 elements)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void *ws = nullptr;
+  if (int rc = scratch_workspace(s, linear3_workspace_bytes(n), &ws)) return rc;
+  return hip_check(launch_linear_scan_3pass(a, b, h0, h, n, ws, s), "linear_scan_3pass launch");
 }
 
 int ssm_copy_f32(const float *src, float *dst, int64_t n, void *stream) {
@@ -284,8 +333,15 @@ int ssm_release_workspace(void) {
     if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = SSM_ERR_HIP;
     (void)hipFree(kv.second.buf);
   }
+  for (auto &kv : g_scratch) {
+    if (!kv.second.buf) continue;
+    (void)hipSetDevice(kv.first.first);
+    if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = SSM_ERR_HIP;
+    (void)hipFree(kv.second.buf);
+  }
   g_linear.clear();
   g_s6.clear();
+  g_scratch.clear();
   (void)hipSetDevice(saved);
   return rc;
 }

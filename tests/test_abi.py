@@ -94,3 +94,14 @@ def test_binding_rejects_host_tensors():
     a = torch.ones(8)
     with pytest.raises(ValueError):
         ssm.linear_scan(a, a)
+
+
+def test_linear_scan_3pass_argument_errors():
+    lib = ssm.load_library()
+    f = lib.ssm_linear_scan_3pass
+    assert f(None, None, 0.0, None, 0, None) == ssm.SSM_OK
+    assert f(FAKE, FAKE, 0.0, FAKE, -1, None) == ssm.SSM_ERR_INVALID_ARG
+    assert f(FAKE, None, 0.0, FAKE, 5, None) == ssm.SSM_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 0.0, FAKE_MISALIGNED, 5, None) == ssm.SSM_ERR_INVALID_ARG
+    assert b"aligned" in lib.ssm_last_error()
+    assert f(FAKE, FAKE, 0.0, FAKE, (1 << 31) + 1, None) == ssm.SSM_ERR_UNSUPPORTED

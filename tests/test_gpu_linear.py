@@ -33,7 +33,8 @@ def test_linear_n65536_workload():
     assert_close(run(a, b).numpy(), ref, TOL, "linear-n65536")
 
 
-# sizes straddling lane chunks (4), rows (256), waves (2048), tiles (8192),
+# sizes straddling lane chunks (4), rows (256), waves (1024; 2048 in the
+# three-pass kernel), tiles (8192),
 # superblocks (64 tiles) and blocks (4096 tiles)
 EDGE_N = [1, 2, 3, 4, 5, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 2047, 2048, 2049,
           4095, 4096, 8191, 8192, 8193, 12289, 65537, 100003, 262144 + 77,
