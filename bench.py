@@ -118,6 +118,27 @@ def bench_linear_3pass(dev, steps, warmup, ms_single):
     }
 
 
+def bench_linear_batched(dev, steps, warmup, nseq=4096, length=32768):
+    """The batched form (independent sequences with their own h0 and h_last)
+    on the same 2^27 elements and distributions, as nseq x length."""
+    import torch
+    import mamba_s6_selective_amd as ssm
+    from mamba_s6_selective_amd.workloads import LINEAR_WORKLOADS, linear_workload_inputs
+    a, b = linear_workload_inputs(LINEAR_WORKLOAD)
+    assert a.numel() == nseq * length
+    a, b = a.to(dev).view(nseq, length), b.to(dev).view(nseq, length)
+    h0 = torch.zeros(nseq, device=dev)
+    h = torch.empty_like(a)
+    last = torch.empty(nseq, device=dev)
+    _, ms_kernel, _ = time_steps(lambda: ssm.linear_scan_batched(a, b, h0, out=h, h_last=last),
+                                 steps, warmup)
+    nbytes = 12 * a.numel() + 8 * nseq
+    return {"workload": f"{LINEAR_WORKLOAD} as {nseq} x {length}",
+            "ms_per_launch": round(ms_kernel, 4),
+            "elements_per_s": a.numel() / (ms_kernel * 1e-3),
+            "achieved_GBs": round(nbytes / (ms_kernel * 1e-3) / 1e9, 1)}
+
+
 def bench_copy(dev, steps, warmup):
     import torch
     import mamba_s6_selective_amd as ssm
@@ -265,6 +286,9 @@ def main():
     record["three_pass"] = bench_linear_3pass(dev, max(5, args.steps // 2), 2, ms_kernel)
     log(f"three-pass: {record['three_pass']['ms_per_launch'] * 1e3:.1f} us, ratio "
         f"{record['three_pass']['measured_ratio']} (model {record['three_pass']['predicted_ratio']})")
+    record["batched"] = bench_linear_batched(dev, max(5, args.steps // 2), 2)
+    log(f"batched: {record['batched']['ms_per_launch'] * 1e3:.1f} us, "
+        f"{record['batched']['achieved_GBs']} GB/s")
     if not args.no_s6:
         record["s6"] = [bench_s6(dev, name, max(5, args.steps // 2), 2, args.exp_cost)
                         for name in S6_BENCH]

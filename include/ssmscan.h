@@ -61,6 +61,30 @@ int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t 
                     void *stream);
 
 /*
+ * Batched form: nseq independent sequences of `len` elements each, stored one
+ * after another (a, b, h are float[nseq][len]), for per-sequence carry-in and
+ * carry-out -- e.g. the cross-chunk carries of a chunked scan, or a long
+ * sequence resumed in pieces ("Selective-scan CUDA kernels", the recurrence
+ * paragraph; the chunked carry scan of "ARM-Scan — Optimized Mamba
+ * Selective-Scan Kernel", "Approach"):
+ *
+ *   h[k][-1] = h0[k];  h[k][t] = a[k][t] * h[k][t-1] + b[k][t]
+ *
+ * h0     : const float[nseq] or NULL (all sequences start from 0).
+ * h_last : float[nseq] or NULL; receives h[k][len-1].
+ * One single-pass launch whatever the shape (the sequences are segments of one
+ * look-back scan). Deterministic. Within this call a multiplier of exactly
+ * zero discards the state before it even when that state is inf or NaN (IEEE
+ * arithmetic, and ssm_linear_scan, would give NaN); this is what keeps one
+ * sequence's non-finite values out of the next.
+ * Errors: SSM_ERR_INVALID_ARG for negative sizes or a null / misaligned a, b,
+ * h with work to do; SSM_ERR_UNSUPPORTED for nseq * len > 2^31; nseq == 0 or
+ * len == 0 is a no-op.
+ */
+int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, float *h,
+                            float *h_last, int64_t nseq, int64_t len, void *stream);
+
+/*
  * The same recurrence and arguments as ssm_linear_scan, computed by the
  * three-pass multi-block design that "Selective-scan CUDA kernels" measures
  * its single-pass look-back against (the introduction's memory-traffic model:

@@ -25,6 +25,7 @@ _P = ctypes.c_void_p
 SIGNATURES = {
     "ssm_linear_scan": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
     "ssm_linear_scan_3pass": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
+    "ssm_linear_scan_batched": (ctypes.c_int, [_P] * 5 + [ctypes.c_int64, ctypes.c_int64, _P]),
     "ssm_selective_scan_fwd": (ctypes.c_int, [_P] * 7 + [ctypes.c_int] * 5 + [_P]),
     "ssm_selective_scan_fwd_bf16": (ctypes.c_int, [_P] * 7 + [ctypes.c_int] * 5 + [_P]),
     "ssm_copy_f32": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
@@ -97,6 +98,40 @@ def _linear_args(a, b, out):
         if out.shape != a.shape:
             raise ValueError("out must match a")
     return out
+
+
+def linear_scan_batched(a, b, h0=None, out=None, h_last=None):
+    """Independent recurrences over the rows of 2-D (nseq, len) fp32 device
+    tensors: h[k][t] = a[k][t]*h[k][t-1] + b[k][t], h[k][-1] = h0[k] (0 when
+    h0 is None). Returns (h, h_last) with h_last[k] = h[k][len-1]."""
+    import torch
+    lib = load_library()
+    _dev_tensor(a, "a", (torch.float32,))
+    _dev_tensor(b, "b", (torch.float32,))
+    if a.shape != b.shape or a.dim() != 2:
+        raise ValueError("a and b must be 2-D (nseq, len) and of equal shape")
+    nseq, length = a.shape
+    if h0 is not None:
+        _dev_tensor(h0, "h0", (torch.float32,))
+        if h0.shape != (nseq,):
+            raise ValueError("h0 must have shape (nseq,)")
+    if out is None:
+        out = torch.empty_like(a)
+    else:
+        _dev_tensor(out, "out", (torch.float32,))
+        if out.shape != a.shape:
+            raise ValueError("out must match a")
+    if h_last is None:
+        h_last = torch.empty(nseq, dtype=torch.float32, device=a.device)
+    else:
+        _dev_tensor(h_last, "h_last", (torch.float32,))
+        if h_last.shape != (nseq,):
+            raise ValueError("h_last must have shape (nseq,)")
+    with torch.cuda.device(a.device):
+        _check(lib.ssm_linear_scan_batched(
+            a.data_ptr(), b.data_ptr(), None if h0 is None else h0.data_ptr(), out.data_ptr(),
+            h_last.data_ptr(), nseq, length, _stream(a)))
+    return out, h_last
 
 
 def linear_scan_3pass(a, b, h0: float = 0.0, out=None):

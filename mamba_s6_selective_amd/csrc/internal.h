@@ -44,10 +44,14 @@ int64_t linear_tile_elems();
 // Enqueues the single-pass scan on min(ntiles, resident_wgs) persistent
 // workgroups. The status levels must hold ntiles, ceil(ntiles/64) and
 // ceil(ntiles/4096) entries whose epochs differ from `epoch`, and
-// ticket[epoch & 1] must be zero.
+// ticket[epoch & 1] must be zero. seg_len > 0 scans n / seg_len independent
+// sequences of seg_len elements (sequence k from seg_h0[k], or 0 if seg_h0 is
+// null; its last value to seg_h_last[k] if that is not null); h0 is then
+// unused. n < 2^32 with segments.
 hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h,
                               int64_t n, int64_t ntiles, LinearStatus status, uint32_t epoch,
-                              int resident_wgs, hipStream_t stream);
+                              int resident_wgs, const float *seg_h0, float *seg_h_last,
+                              uint32_t seg_len, hipStream_t stream);
 // Workgroups of the scan kernel that fit on one CU at once (0 on error).
 int linear_wgs_per_cu();
 

@@ -49,6 +49,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 #include "scan_common.h"
 
@@ -83,13 +85,14 @@ __device__ __forceinline__ bool word_ready(uint64_t w, uint32_t epoch) {
 // Composition, in lane order, of the pairs held by lanes [0, count) of the
 // wave (later lanes contribute the identity). Fixed DPP tree: the result
 // depends only on the values and `count`. Returned in every lane.
+template <class Op>
 __device__ __forceinline__ void window_total(float a, float b, int count, int lane, float &ta,
                                              float &tb) {
   if (lane >= count) {
     a = 1.0f;
     b = 0.0f;
   }
-  wave_scan(a, b);
+  wave_scan<Op>(a, b);
   ta = lane_f(a, 63);
   tb = lane_f(b, 63);
 }
@@ -179,27 +182,27 @@ __device__ __forceinline__ bool lb_done(const LookBack &s) {
 
 // Composition of the complete look-back windows (fixed shapes: the result
 // depends only on the words and the tile index).
+template <class Op>
 __device__ Prefix lb_finish(const LookBack &s, float h0, int lane) {
   float p2a, p2b, pba, pbb;
-  window_total(payload(s.w2a), payload(s.w2b), s.n2, lane, p2a, p2b);
-  window_total(payload(s.w1a), payload(s.w1b), s.n1, lane, pba, pbb);
+  window_total<Op>(payload(s.w2a), payload(s.w2b), s.n2, lane, p2a, p2b);
+  window_total<Op>(payload(s.w1a), payload(s.w1b), s.n1, lane, pba, pbb);
   Prefix pf;
 #pragma unroll
   for (int q = 0; q < kRecent; ++q) {
     if (q < s.nw - 1) {  // a whole earlier superblock
       float qa, qb;
-      window_total(payload(s.wa[q]), payload(s.wb[q]), kFan, lane, qa, qb);
-      pbb = __builtin_fmaf(qa, pbb, qb);
-      pba *= qa;
+      window_total<Op>(payload(s.wa[q]), payload(s.wb[q]), kFan, lane, qa, qb);
+      Op::compose(pba, pbb, qa, qb, pba, pbb);
     } else if (q == s.nw - 1) {  // the tile's own superblock, up to the tile
-      window_total(payload(s.wa[q]), payload(s.wb[q]), s.n0, lane, pf.p0a, pf.p0b);
+      window_total<Op>(payload(s.wa[q]), payload(s.wb[q]), s.n0, lane, pf.p0a, pf.p0b);
     }
   }
   pf.pba = pba;
   pf.pbb = pbb;
-  const float h2 = __builtin_fmaf(p2a, h0, p2b);
-  const float h1 = __builtin_fmaf(pba, h2, pbb);
-  pf.h_in = __builtin_fmaf(pf.p0a, h1, pf.p0b);
+  const float h2 = Op::apply(p2a, h0, p2b);
+  const float h1 = Op::apply(pba, h2, pbb);
+  pf.h_in = Op::apply(pf.p0a, h1, pf.p0b);
   return pf;
 }
 
@@ -207,26 +210,63 @@ __device__ Prefix lb_finish(const LookBack &s, float h0, int lane) {
 // superblock publishes the superblock's aggregate (level 1), and the last tile
 // of a block the block's aggregate (level 2). For the last tile of a block,
 // blk1 is its own block, so PB (+) P0 (+) own covers the whole block.
+template <class Op>
 __device__ __forceinline__ void publish_higher(const LinearStatus &st, int64_t tile,
                                                const Prefix &pf, float ga, float gb,
                                                uint32_t epoch, int lane) {
   const int64_t sb = tile / kFan;
   const int64_t blk = sb / kFan;
   if (tile - sb * kFan != kFan - 1 || lane != 0) return;
-  const float sbb = __builtin_fmaf(ga, pf.p0b, gb);  // P0 (+) own aggregate
-  const float sba = pf.p0a * ga;
+  float sba, sbb;
+  Op::compose(pf.p0a, pf.p0b, ga, gb, sba, sbb);  // P0 (+) own aggregate
   st_status(&st.lvl1[sb].a, epoch, sba);
   st_status(&st.lvl1[sb].b, epoch, sbb);
   if (sb - blk * kFan == kFan - 1) {
-    st_status(&st.lvl2[blk].a, epoch, pf.pba * sba);
-    st_status(&st.lvl2[blk].b, epoch, __builtin_fmaf(sba, pf.pbb, sbb));
+    float ba, bb;
+    Op::compose(pf.pba, pf.pbb, sba, sbb, ba, bb);
+    st_status(&st.lvl2[blk].a, epoch, ba);
+    st_status(&st.lvl2[blk].b, epoch, bb);
   }
 }
 
+// Independent sequences inside one scan (the batched form): `len` elements
+// each, sequence k starting from h0[k] (0 if h0 is null) and, when h_last is
+// not null, leaving its last value in h_last[k]. len == 0: one sequence.
+// i / len is evaluated as (t1 + ((i - t1) >> sh1)) >> sh2 with
+// t1 = mulhi(magic, i), the round-up method for division by an invariant
+// integer (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994), exact for every 32-bit i.
+struct Segments {
+  const float *h0;
+  float *h_last;
+  uint32_t len, magic, sh1, sh2;
+};
+
+// Position t of element i within its sequence, and the sequence's index k
+// (i < 2^32; len >= 1).
+__device__ __forceinline__ void seg_pos(uint32_t i, const Segments &sg, uint32_t &k,
+                                        uint32_t &t) {
+  const uint32_t t1 = __umulhi(sg.magic, i);
+  k = (t1 + ((i - t1) >> sg.sh1)) >> sg.sh2;
+  t = i - k * sg.len;
+}
+
+// Whether the 4 elements from i on hold the first or the last element of a
+// sequence (then each is looked at separately).
+__device__ __forceinline__ bool seg_edge(uint32_t i, const Segments &sg) {
+  uint32_t k, t;
+  seg_pos(i, sg, k, t);
+  return t == 0 || t + 4 >= sg.len;
+}
+
 // Loads one tile (rows of float4 per wave); past n the identity map (1, 0).
+// With segments, the first element of every sequence becomes the constant
+// map (0, a*h0 + b): it ignores whatever precedes it.
+template <bool Seg>
 __device__ __forceinline__ void load_tile(const float *__restrict__ a,
                                           const float *__restrict__ b, int64_t n, int64_t tile,
-                                          float4 (&va)[kRows], float4 (&vb)[kRows]) {
+                                          const Segments &sg, float4 (&va)[kRows],
+                                          float4 (&vb)[kRows]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t wave_start = tile * kTileElems + int64_t(wave) * kWaveElems;
@@ -252,10 +292,34 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ a,
       vb[r] = make_float4(tb[0], tb[1], tb[2], tb[3]);
     }
   }
+  if constexpr (Seg) {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int64_t off = wave_start + r * kRowElems + lane * 4;
+      if (off < n && seg_edge(uint32_t(off), sg)) {
+        float ta[4] = {va[r].x, va[r].y, va[r].z, va[r].w};
+        float tb[4] = {vb[r].x, vb[r].y, vb[r].z, vb[r].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (off + j < n) {
+            uint32_t k, t;
+            seg_pos(uint32_t(off + j), sg, k, t);
+            if (t == 0) {
+              tb[j] = __builtin_fmaf(ta[j], sg.h0 ? sg.h0[k] : 0.0f, tb[j]);
+              ta[j] = 0.0f;
+            }
+          }
+        }
+        va[r] = make_float4(ta[0], ta[1], ta[2], ta[3]);
+        vb[r] = make_float4(tb[0], tb[1], tb[2], tb[3]);
+      }
+    }
+  }
 }
 
 // Data waves, phase 1: chunk aggregates of the lane's 4 items per row, a wave
 // scan per row, and the wave's aggregate (rows folded in order) into LDS.
+template <class Op>
 __device__ __forceinline__ void tile_local_scan(const float4 (&va)[kRows],
                                                 const float4 (&vb)[kRows], float (&ia)[kRows],
                                                 float (&ib)[kRows], float *s_wave_a,
@@ -265,10 +329,10 @@ __device__ __forceinline__ void tile_local_scan(const float4 (&va)[kRows],
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
     float ca = va[r].x, cb = vb[r].x;
-    cb = __builtin_fmaf(va[r].y, cb, vb[r].y); ca *= va[r].y;
-    cb = __builtin_fmaf(va[r].z, cb, vb[r].z); ca *= va[r].z;
-    cb = __builtin_fmaf(va[r].w, cb, vb[r].w); ca *= va[r].w;
-    wave_scan(ca, cb);
+    Op::compose(ca, cb, va[r].y, vb[r].y, ca, cb);
+    Op::compose(ca, cb, va[r].z, vb[r].z, ca, cb);
+    Op::compose(ca, cb, va[r].w, vb[r].w, ca, cb);
+    wave_scan<Op>(ca, cb);
     ia[r] = ca;
     ib[r] = cb;
   }
@@ -276,8 +340,7 @@ __device__ __forceinline__ void tile_local_scan(const float4 (&va)[kRows],
 #pragma unroll
   for (int r = 1; r < kRows; ++r) {
     const float ra = lane_f(ia[r], 63), rb = lane_f(ib[r], 63);
-    wb = __builtin_fmaf(ra, wb, rb);
-    wa *= ra;
+    Op::compose(wa, wb, ra, rb, wa, wb);
   }
   if (lane == 0) {
     s_wave_a[wave] = wa;
@@ -286,24 +349,26 @@ __device__ __forceinline__ void tile_local_scan(const float4 (&va)[kRows],
 }
 
 // Data waves, phase 2: carry into each row, then into each lane's chunk, then
-// re-run the recurrence over the lane's 4 items and store.
+// re-run the recurrence over the lane's 4 items and store (with segments,
+// the last value of each sequence also goes to h_last).
+template <bool Seg, class Op>
 __device__ __forceinline__ void tile_apply(const float4 (&va)[kRows], const float4 (&vb)[kRows],
                                            const float (&ia)[kRows], const float (&ib)[kRows],
                                            float c, float *__restrict__ h, int64_t n,
-                                           int64_t tile) {
+                                           int64_t tile, const Segments &sg) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t wave_start = tile * kTileElems + int64_t(wave) * kWaveElems;
   const bool full = (tile + 1) * kTileElems <= n;
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
-    const float end = __builtin_fmaf(ia[r], c, ib[r]);      // h after this lane's chunk
+    const float end = Op::apply(ia[r], c, ib[r]);           // h after this lane's chunk
     const float cin = dpp<kWaveShr1, 0xf, 0xf>(c, end);     // h before it
     float4 o;
-    o.x = __builtin_fmaf(va[r].x, cin, vb[r].x);
-    o.y = __builtin_fmaf(va[r].y, o.x, vb[r].y);
-    o.z = __builtin_fmaf(va[r].z, o.y, vb[r].z);
-    o.w = __builtin_fmaf(va[r].w, o.z, vb[r].w);
+    o.x = Op::apply(va[r].x, cin, vb[r].x);
+    o.y = Op::apply(va[r].y, o.x, vb[r].y);
+    o.z = Op::apply(va[r].z, o.y, vb[r].z);
+    o.w = Op::apply(va[r].w, o.z, vb[r].w);
     const int64_t off = wave_start + r * kRowElems + lane * 4;
     if (full) {
       store_nt(h + off, o);
@@ -312,6 +377,19 @@ __device__ __forceinline__ void tile_apply(const float4 (&va)[kRows], const floa
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (off + j < n) h[off + j] = ov[j];
+    }
+    if constexpr (Seg) {
+      if (sg.h_last && off < n && seg_edge(uint32_t(off), sg)) {
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (off + j < n) {
+            uint32_t k, t;
+            seg_pos(uint32_t(off + j), sg, k, t);
+            if (t == sg.len - 1) sg.h_last[k] = ov[j];
+          }
+        }
+      }
     }
     c = lane_f(end, 63);
   }
@@ -381,13 +459,14 @@ __device__ __forceinline__ void unpark(const Shared &sh, int slot, float4 (&va)[
 // Data waves: local scan of a loaded tile; the last data wave to finish folds
 // the wave aggregates into the tile aggregate and publishes it (level 0) at
 // once, without waiting for any other workgroup.
+template <class Op>
 __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
                                                  const float4 (&vb)[kRows], float (&ia)[kRows],
                                                  float (&ib)[kRows], Shared &sh, int ring, int slot,
                                                  const LinearStatus &st, int64_t tile,
                                                  uint32_t epoch) {
   const int lane = threadIdx.x & 63;
-  tile_local_scan(va, vb, ia, ib, sh.wave_a[ring], sh.wave_b[ring]);
+  tile_local_scan<Op>(va, vb, ia, ib, sh.wave_a[ring], sh.wave_b[ring]);
   unsigned prior = 0;
   if (lane == 0)
     prior = __hip_atomic_fetch_add(&sh.arrived[slot], 1u, __ATOMIC_ACQ_REL,
@@ -397,8 +476,7 @@ __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
     float ga = sh.wave_a[ring][0], gb = sh.wave_b[ring][0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      gb = __builtin_fmaf(sh.wave_a[ring][w], gb, sh.wave_b[ring][w]);
-      ga *= sh.wave_a[ring][w];
+      Op::compose(ga, gb, sh.wave_a[ring][w], sh.wave_b[ring][w], ga, gb);
     }
     if (lane == 0) {
       st_status(&st.lvl0[tile].a, epoch, ga);
@@ -444,9 +522,12 @@ __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
 // finish, however many workgroups the device keeps resident.
 // The ticket of a launch is st.ticket[epoch & 1]; the first workgroup zeroes
 // the other slot for the next launch on the stream.
+template <bool Seg>
 __global__ __launch_bounds__(kThreads + 64) void linear_scan_kernel(
     const float *__restrict__ a, const float *__restrict__ b, float h0,
-    float *__restrict__ h, int64_t n, int64_t ntiles, LinearStatus st, uint32_t epoch) {
+    float *__restrict__ h, int64_t n, int64_t ntiles, LinearStatus st, uint32_t epoch,
+    Segments sg) {
+  using Op = typename std::conditional<Seg, ResetOp, PlainOp>::type;
   __shared__ Shared sh;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -486,13 +567,13 @@ __global__ __launch_bounds__(kThreads + 64) void linear_scan_kernel(
           lb_check(lp, epoch);
         }
         const int rp = (j - 1) & 3;
-        const Prefix pf = lb_finish(lp, h0, lane);
-        publish_higher(st, tp, pf, sh.tile_a[rp], sh.tile_b[rp], epoch, lane);
+        const Prefix pf = lb_finish<Op>(lp, h0, lane);
+        publish_higher<Op>(st, tp, pf, sh.tile_a[rp], sh.tile_b[rp], epoch, lane);
         if (lane == 0) {
           float c = pf.h_in;
           for (int w = 0; w < kWaves; ++w) {
             sh.carry[rp][w] = c;
-            c = __builtin_fmaf(sh.wave_a[rp][w], c, sh.wave_b[rp][w]);
+            c = Op::apply(sh.wave_a[rp][w], c, sh.wave_b[rp][w]);
           }
         }
       }
@@ -519,10 +600,10 @@ __global__ __launch_bounds__(kThreads + 64) void linear_scan_kernel(
   // scanned, (ma, mb) tile being loaded; prefixes of the two parked tiles.
   float4 va[kRows], vb[kRows], na[kRows], nb[kRows];
   float iap[kRows], ibp[kRows], iaw[kRows], ibw[kRows];
-  if (t0 < ntiles) load_tile(a, b, n, t0, va, vb);
-  if (t1 < ntiles) load_tile(a, b, n, t1, na, nb);
+  if (t0 < ntiles) load_tile<Seg>(a, b, n, t0, sg, va, vb);
+  if (t1 < ntiles) load_tile<Seg>(a, b, n, t1, sg, na, nb);
   if (t0 < ntiles) {
-    scan_and_publish(va, vb, iaw, ibw, sh, 0, 0, st, t0, epoch);
+    scan_and_publish<Op>(va, vb, iaw, ibw, sh, 0, 0, st, t0, epoch);
     park(sh, 0, va, vb);
   }
   __syncthreads();  // B
@@ -531,15 +612,15 @@ __global__ __launch_bounds__(kThreads + 64) void linear_scan_kernel(
     int64_t claimed = ntiles;
     if (wave == 0 && t2 < ntiles) claimed = successor(t2, ntiles, ticket, lane);
     float4 ma[kRows], mb[kRows];
-    if (t2 < ntiles) load_tile(a, b, n, t2, ma, mb);
+    if (t2 < ntiles) load_tile<Seg>(a, b, n, t2, sg, ma, mb);
     float nia[kRows], nib[kRows];
     if (t1 < ntiles)
-      scan_and_publish(na, nb, nia, nib, sh, (j + 1) & 3, (j + 1) & 1, st, t1, epoch);
+      scan_and_publish<Op>(na, nb, nia, nib, sh, (j + 1) & 3, (j + 1) & 1, st, t1, epoch);
     if (wave == 0 && lane == 0) sh.ids[(j + 3) & 3] = claimed;
     __syncthreads();  // C_j
     if (tp < ntiles) {
       unpark(sh, (j + 1) & 1, va, vb);  // t_{j-1} sits in slot (j - 1) % 2
-      tile_apply(va, vb, iap, ibp, sh.carry[(j - 1) & 3][wave], h, n, tp);
+      tile_apply<Seg, Op>(va, vb, iap, ibp, sh.carry[(j - 1) & 3][wave], h, n, tp, sg);
     }
     if (t1 < ntiles) park(sh, (j + 1) & 1, na, nb);
 #pragma unroll
@@ -574,20 +655,36 @@ int64_t linear_tile_elems() { return kTileElems; }
 
 hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h,
                               int64_t n, int64_t ntiles, LinearStatus status, uint32_t epoch,
-                              int resident_wgs, hipStream_t stream) {
+                              int resident_wgs, const float *seg_h0, float *seg_h_last,
+                              uint32_t seg_len, hipStream_t stream) {
   const unsigned grid = unsigned(ntiles < resident_wgs ? ntiles : resident_wgs);
-  hipLaunchKernelGGL(linear_scan_kernel, dim3(grid), dim3(kThreads + 64), 0, stream, a, b, h0,
-                     h, n, ntiles, status, epoch);
+  Segments sg{seg_h0, seg_h_last, seg_len, 0, 0, 0};
+  if (seg_len > 0) {  // magic number for division by seg_len (see Segments)
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < seg_len) ++l;
+    sg.magic = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - seg_len)) / seg_len + 1);
+    sg.sh1 = l < 1 ? l : 1;
+    sg.sh2 = l > 0 ? l - 1 : 0;
+  }
+  if (seg_len == 0)
+    hipLaunchKernelGGL(linear_scan_kernel<false>, dim3(grid), dim3(kThreads + 64), 0, stream, a,
+                       b, h0, h, n, ntiles, status, epoch, sg);
+  else
+    hipLaunchKernelGGL(linear_scan_kernel<true>, dim3(grid), dim3(kThreads + 64), 0, stream, a,
+                       b, h0, h, n, ntiles, status, epoch, sg);
   return hipGetLastError();
 }
 
 int linear_wgs_per_cu() {
-  int per_cu = 0;
+  int plain = 0, seg = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void *>(linear_scan_kernel), kThreads + 64, 0) !=
-      hipSuccess)
+          &plain, reinterpret_cast<const void *>(linear_scan_kernel<false>), kThreads + 64, 0) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &seg, reinterpret_cast<const void *>(linear_scan_kernel<true>), kThreads + 64, 0) !=
+          hipSuccess)
     return 0;
-  return per_cu;
+  return plain < seg ? plain : seg;
 }
 
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t stream) {

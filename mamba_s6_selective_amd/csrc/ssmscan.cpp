@@ -223,8 +223,32 @@ int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t 
   int grid = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int rc = linear_workspace(s, ntiles, &status, &epoch, &grid)) return rc;
-  return hip_check(launch_linear_scan(a, b, h0, h, n, ntiles, status, epoch, grid, s),
+  return hip_check(launch_linear_scan(a, b, h0, h, n, ntiles, status, epoch, grid, nullptr,
+                                      nullptr, 0, s),
                    "linear_scan launch");
+}
+
+int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, float *h,
+                            float *h_last, int64_t nseq, int64_t len, void *stream) {
+  g_last_error.clear();
+  if (nseq < 0 || len < 0) return fail(SSM_ERR_INVALID_ARG, "nseq and len must be >= 0");
+  if (nseq == 0 || len == 0) return SSM_OK;
+  if (!a || !b || !h) return fail(SSM_ERR_INVALID_ARG, "null a, b or h with work to do");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(h))
+    return fail(SSM_ERR_INVALID_ARG, "a, b and h must be 16-byte aligned");
+  if (nseq > (int64_t(1) << 31) / len)
+    return fail(SSM_ERR_UNSUPPORTED, "nseq * len too large for one launch (max 2^31 elements)");
+  const int64_t n = nseq * len;
+  const int64_t tile = linear_tile_elems();
+  const int64_t ntiles = (n + tile - 1) / tile;
+  LinearStatus status{};
+  uint32_t epoch = 0;
+  int grid = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int rc = linear_workspace(s, ntiles, &status, &epoch, &grid)) return rc;
+  return hip_check(launch_linear_scan(a, b, 0.0f, h, n, ntiles, status, epoch, grid, h0, h_last,
+                                      uint32_t(len), s),
+                   "linear_scan_batched launch");
 }
 
 int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, int64_t n,

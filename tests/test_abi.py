@@ -105,3 +105,16 @@ def test_linear_scan_3pass_argument_errors():
     assert f(FAKE, FAKE, 0.0, FAKE_MISALIGNED, 5, None) == ssm.SSM_ERR_INVALID_ARG
     assert b"aligned" in lib.ssm_last_error()
     assert f(FAKE, FAKE, 0.0, FAKE, (1 << 31) + 1, None) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_linear_scan_batched_argument_errors():
+    lib = ssm.load_library()
+    f = lib.ssm_linear_scan_batched
+    assert f(None, None, None, None, None, 0, 10, None) == ssm.SSM_OK
+    assert f(None, None, None, None, None, 10, 0, None) == ssm.SSM_OK
+    assert f(FAKE, FAKE, None, FAKE, None, -1, 10, None) == ssm.SSM_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, FAKE, None, 10, -1, None) == ssm.SSM_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, None, None, 2, 3, None) == ssm.SSM_ERR_INVALID_ARG
+    assert f(FAKE_MISALIGNED, FAKE, None, FAKE, None, 2, 3, None) == ssm.SSM_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, FAKE, None, 1 << 20, (1 << 11) + 1, None) == \
+        ssm.SSM_ERR_UNSUPPORTED
