@@ -23,6 +23,9 @@ widened exactly from fp32 or bf16):
   Selective-Scan Kernel" (sections "Approach" and "What broke"): the reverse
   recurrence reuses the same discretized terms, and the fused result must equal
   the two independent scans.
+* ``s6.softplus``: log(1 + exp(x)), which the same transcript's model applies
+  to the delta projection (with its bias) before the scan; ``selective_scan``
+  applies it itself when asked to (delta_softplus=True, delta_bias).
 * ``native``: a plain C twin of the same loops (``oracle_c.c``) used where the
   Python loops would be too slow (full-size parity checks, the CPU baseline).
 
@@ -30,4 +33,4 @@ Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, exact rational brute force and invariants (not against itself).
 """
 from .linear import linear_scan, affine_combine, affine_prefix, apply_affine  # noqa: F401
-from .s6 import selective_scan  # noqa: F401
+from .s6 import selective_scan, softplus  # noqa: F401

@@ -11,9 +11,16 @@ Sources:
   "What broke": a reverse recurrence that shares the forward one's discretized
   terms, fused with it, and equal to two independent scans.
 
+* The same transcript's model computes delta = softplus(proj_delta(x)), the
+  projection carrying a bias, with softplus(x) = log(1 + exp(x)) evaluated by
+  the log1p-exp trick.
+
 Readings (where the pages are silent):
-* u is the transcript's x; delta is passed after softplus (the kernel does not
-  apply softplus).
+* u is the transcript's x; by default delta is passed after softplus and used
+  as given. With delta_softplus=True the scan applies softplus to
+  delta + delta_bias[d] itself (the bias being the projection's, added before
+  the softplus); delta_bias alone (without softplus) is not a form the pages
+  use and is rejected.
 * reverse: h_r[L] = 0 and h_r[t] = dA[t]*h_r[t+1] + x_db[t] for t = L-1 .. 0,
   with the same dA[t], x_db[t] as the forward pass; y_r[t] = sum_n C[t]*h_r[t] + D*u[t].
 * bidirectional: y = y_fwd + y_rev, each with its own D*u term, so D*u counts
@@ -24,6 +31,12 @@ from __future__ import annotations
 import numpy as np
 
 DIRECTIONS = ("fwd", "rev", "bidir")
+
+
+def softplus(x) -> np.ndarray:
+    """log(1 + exp(x)) in float64, by numpy's logaddexp(0, x) (exact for large
+    |x|: no overflow for x >> 0, no cancellation for x << 0)."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
 
 
 def _one_direction(u, delta, A, B, C, D, reverse: bool) -> np.ndarray:
@@ -43,15 +56,25 @@ def _one_direction(u, delta, A, B, C, D, reverse: bool) -> np.ndarray:
     return y
 
 
-def selective_scan(u, delta, A, B, C, D, direction: str = "fwd") -> np.ndarray:
+def selective_scan(u, delta, A, B, C, D, direction: str = "fwd", delta_bias=None,
+                   delta_softplus: bool = False) -> np.ndarray:
     """S6 output y of shape (batch, L, d_inner), float64.
 
     u, delta: (batch, L, d_inner); A: (d_inner, N); B, C: (batch, L, N);
-    D: (d_inner,). Any float dtype; everything is widened to float64 first.
-    Loops over t in Python and vectorises over (batch, d_inner, N).
+    D: (d_inner,); delta_bias: (d_inner,) or None. Any float dtype; everything
+    is widened to float64 first. With delta_softplus, delta is replaced by
+    softplus(delta + delta_bias) before the scan. Loops over t in Python and
+    vectorises over (batch, d_inner, N).
     """
     if direction not in DIRECTIONS:
         raise ValueError(f"direction must be one of {DIRECTIONS}")
+    if delta_bias is not None and not delta_softplus:
+        raise ValueError("delta_bias is only applied together with delta_softplus")
+    if delta_softplus:
+        delta = np.asarray(delta, dtype=np.float64)
+        if delta_bias is not None:
+            delta = delta + np.asarray(delta_bias, dtype=np.float64)[None, None, :]
+        delta = softplus(delta)
     u = np.asarray(u, dtype=np.float64)
     delta = np.asarray(delta, dtype=np.float64)
     A = np.asarray(A, dtype=np.float64)

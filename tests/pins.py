@@ -12,6 +12,7 @@ import math
 import random
 from fractions import Fraction
 
+import mpmath
 import numpy as np
 
 # --------------------------------------------------------------------------
@@ -331,3 +332,46 @@ def s6_pin_failures(s6, linear_scan):
         if not ok:
             fails.append(name)
     return fails
+
+
+# ---------------------------------------------------------------- softplus ---
+#
+# softplus(x) = log(1 + exp(x)), which the POPCORNBENCH transcript's model
+# applies to the delta projection (bias included) before the scan.
+
+def softplus_pin_failures(softplus):
+    """softplus(x) -> float64 array. Returns names of failed pins."""
+    fails = []
+    sp = _guard(softplus)
+    rs = np.random.RandomState(11)
+    x = np.concatenate([rs.normal(scale=4.0, size=200), [-60.0, -30.0, -1e-9, 1e-9, 30.0]])
+    checks = {
+        # log 2 at zero
+        "value_at_zero": lambda: abs(float(sp(np.array([0.0]))[0]) - math.log(2.0)) <= 1e-15,
+        # log(1 + e^x) - log(1 + e^-x) = log(e^x) = x
+        "odd_part_is_x": lambda: _close(sp(x) - sp(-x), x, 1e-13),
+        # softplus(x) = e^x - e^2x / 2 + ... for x << 0: relatively within e^x + rounding
+        "small_tail": lambda: bool(np.all(
+            np.abs(sp(np.array([-30.0, -40.0, -700.0])) / np.exp([-30.0, -40.0, -700.0]) - 1.0)
+            <= 1e-15 + np.exp([-30.0, -40.0, -700.0]))),
+        # softplus(x) = x + e^-x - ... for x >> 0, and no overflow
+        "large_tail": lambda: _close(sp(np.array([50.0, 1000.0])), [50.0, 1000.0], 1e-15),
+        # against 50-digit log(1 + exp(x)) at a few points
+        "mpmath_values": lambda: _softplus_vs_mpmath(sp),
+    }
+    for name, check in checks.items():
+        try:
+            ok = check()
+        except _Crashed:
+            ok = False
+        if not ok:
+            fails.append(name)
+    return fails
+
+
+def _softplus_vs_mpmath(sp):
+    mpmath.mp.dps = 50
+    pts = [-20.0, -3.5, -0.25, 0.0, 0.7, 2.0, 9.0, 35.0]
+    got = sp(np.array(pts))
+    ref = [float(mpmath.log(1 + mpmath.exp(mpmath.mpf(p)))) for p in pts]
+    return _close(got, ref, 1e-14)

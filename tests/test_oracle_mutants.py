@@ -154,3 +154,21 @@ def test_unmutated_copy_passes():
 @pytest.mark.parametrize("name", S6_MUTANTS)
 def test_s6_mutant_is_caught(name):
     assert s6_pin_failures(_s6_mutant(name), oracle.linear_scan) != [], name
+
+
+# -------------------------------------------------------------- softplus ---
+
+SOFTPLUS_MUTANTS = {
+    "naive_overflow": lambda x: np.log(1.0 + np.exp(np.asarray(x, dtype=np.float64))),
+    "missing_exp": lambda x: np.log1p(np.abs(np.asarray(x, dtype=np.float64))),
+    "wrong_sign": lambda x: np.logaddexp(0.0, -np.asarray(x, dtype=np.float64)),
+    "relu_only": lambda x: np.maximum(np.asarray(x, dtype=np.float64), 0.0),
+    "log2_base": lambda x: np.logaddexp2(0.0, np.asarray(x, dtype=np.float64)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SOFTPLUS_MUTANTS))
+def test_softplus_mutant_is_caught(name):
+    from pins import softplus_pin_failures
+    with np.errstate(all="ignore"):
+        assert softplus_pin_failures(SOFTPLUS_MUTANTS[name]) != [], name
