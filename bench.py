@@ -191,6 +191,21 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
         ssm.selective_scan_fwd(*t[:6], direction=w["direction"], out=t[6])
 
     ms_step, ms_kernel, ms_min = time_steps(step, steps, warmup)
+    fused = None
+    if w["direction"] == "fwd" and w["dtype"] == "bf16":
+        # the same scan with delta given before its activation and softplus fused in
+        pre = [inp.delta_pre.to(dev).clone() for _ in range(sets)]
+
+        def step_fused():
+            t = bufs[k[0] % sets]
+            ssm.selective_scan_fwd(t[0], pre[k[0] % sets], *t[2:6], direction=w["direction"],
+                                   out=t[6], delta_softplus=True)
+            k[0] += 1
+
+        _, ms_fused, _ = time_steps(step_fused, steps, warmup)
+        fused = {"ms_kernel_avg": round(ms_fused, 4),
+                 "ratio_to_unfused": round(ms_fused / ms_kernel, 3),
+                 "separate_pass_bytes": 2 * E * (2 if w["dtype"] == "bf16" else 4)}
     lane_cycles = tdn * (other + exp_cost)
     alu_frac = lane_cycles / (ms_kernel * 1e-3) / (VALU_PEAK_T * 1e12)
     gbs = nbytes / (ms_kernel * 1e-3) / 1e9
@@ -203,6 +218,7 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
                      "traffic": None},
         "hbm": {"achieved_GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4),
                 "algorithmic_bytes": nbytes},
+        "fused_softplus": fused,
     }
 
 

@@ -140,6 +140,35 @@ int ssm_selective_scan_fwd_bf16(const uint16_t *u, const uint16_t *delta,
                                 const float *D, float *y, int batch, int L,
                                 int d_inner, int N, int direction, void *stream);
 
+/* Flags of ssm_selective_scan_fwd_ex. */
+enum {
+  SSM_FLAG_BF16 = 1,           /* u, delta, B, C are bfloat16 (raw uint16 bits) */
+  SSM_FLAG_DELTA_SOFTPLUS = 2  /* delta <- softplus(delta + delta_bias[d]) as read */
+};
+
+/*
+ * S6 selective scan with the input activation of delta fused in. The
+ * POPCORNBENCH transcript FW-GLM-5-1 (level 2, problem 30) computes
+ * delta = softplus(proj_delta(x)) (the projection carrying a bias) before the
+ * scan; with SSM_FLAG_DELTA_SOFTPLUS the scan takes the pre-activation values
+ * and applies  delta_eff[b,t,d] = log(1 + exp(delta[b,t,d] + delta_bias[d]))
+ * itself as it reads them, so the activated delta never goes through memory.
+ * Everything else is as ssm_selective_scan_fwd (fp32 inputs) or
+ * ssm_selective_scan_fwd_bf16 (SSM_FLAG_BF16).
+ *
+ * delta_bias : const float[d_inner] or NULL (no bias); only with
+ *              SSM_FLAG_DELTA_SOFTPLUS.
+ * flags      : OR of SSM_FLAG_*.
+ * softplus is evaluated in fp32 as max(x, 0) + log(1 + exp(-|x|)), with a
+ * short series where exp(-|x|) < 2^-6.
+ * Errors: as ssm_selective_scan_fwd; SSM_ERR_INVALID_ARG also for unknown
+ * flag bits and for delta_bias without SSM_FLAG_DELTA_SOFTPLUS.
+ */
+int ssm_selective_scan_fwd_ex(const void *u, const void *delta, const float *delta_bias,
+                              const float *A, const void *B, const void *C, const float *D,
+                              float *y, int batch, int L, int d_inner, int N, int direction,
+                              unsigned flags, void *stream);
+
 /*
  * Device copy dst[i] = src[i], i < n (fp32). A known-simple streaming kernel
  * used by measurement code as the bandwidth reference and as the sentinel

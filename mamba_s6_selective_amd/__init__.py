@@ -14,6 +14,9 @@ LIB_PATH = PKG / "libssmscan.so"
 
 DIRECTIONS = {"fwd": 0, "rev": 1, "bidir": 2}
 
+SSM_FLAG_BF16 = 1
+SSM_FLAG_DELTA_SOFTPLUS = 2
+
 SSM_OK = 0
 SSM_ERR_INVALID_ARG = -1
 SSM_ERR_UNSUPPORTED = -2
@@ -28,6 +31,8 @@ SIGNATURES = {
     "ssm_linear_scan_batched": (ctypes.c_int, [_P] * 5 + [ctypes.c_int64, ctypes.c_int64, _P]),
     "ssm_selective_scan_fwd": (ctypes.c_int, [_P] * 7 + [ctypes.c_int] * 5 + [_P]),
     "ssm_selective_scan_fwd_bf16": (ctypes.c_int, [_P] * 7 + [ctypes.c_int] * 5 + [_P]),
+    "ssm_selective_scan_fwd_ex": (ctypes.c_int, [_P] * 8 + [ctypes.c_int] * 5 +
+                                  [ctypes.c_uint, _P]),
     "ssm_copy_f32": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
     "ssm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ssm_last_error": (ctypes.c_char_p, []),
@@ -165,9 +170,12 @@ def linear_scan(a, b, h0: float = 0.0, out=None):
     return out
 
 
-def selective_scan_fwd(u, delta, A, B, C, D, direction: str = "fwd", out=None):
+def selective_scan_fwd(u, delta, A, B, C, D, direction: str = "fwd", out=None,
+                       delta_bias=None, delta_softplus: bool = False):
     """S6 scan. u, delta: (batch, L, d); A: (d, N) fp32; B, C: (batch, L, N);
-    D: (d,) fp32. u, delta, B, C all fp32 or all bf16. Returns y (fp32)."""
+    D: (d,) fp32. u, delta, B, C all fp32 or all bf16. Returns y (fp32).
+    With delta_softplus, delta holds pre-activation values and the scan uses
+    softplus(delta + delta_bias[d]) (delta_bias: (d,) fp32 or None)."""
     import torch
     lib = load_library()
     if direction not in DIRECTIONS:
@@ -192,6 +200,20 @@ def selective_scan_fwd(u, delta, A, B, C, D, direction: str = "fwd", out=None):
         _dev_tensor(out, "out", (torch.float32,))
         if out.shape != u.shape:
             raise ValueError("out must have u's shape")
+    if delta_bias is not None:
+        _dev_tensor(delta_bias, "delta_bias", (torch.float32,))
+        if delta_bias.shape != (d,):
+            raise ValueError("delta_bias must have shape (d,)")
+    if delta_softplus or delta_bias is not None:
+        flags = (SSM_FLAG_BF16 if dt == torch.bfloat16 else 0) | \
+            (SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0)
+        with torch.cuda.device(u.device):
+            _check(lib.ssm_selective_scan_fwd_ex(
+                u.data_ptr(), delta.data_ptr(),
+                None if delta_bias is None else delta_bias.data_ptr(), A.data_ptr(),
+                B.data_ptr(), C.data_ptr(), D.data_ptr(), out.data_ptr(), batch, L, d, N,
+                DIRECTIONS[direction], flags, _stream(u)))
+        return out
     fn = lib.ssm_selective_scan_fwd if dt == torch.float32 else lib.ssm_selective_scan_fwd_bf16
     with torch.cuda.device(u.device):
         _check(fn(u.data_ptr(), delta.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(),

@@ -19,6 +19,8 @@ struct S6Args {
   float *y;           // (batch, L, d_inner)
   int batch, L, d_inner, N, direction;
   bool bf16;
+  bool delta_softplus;       // delta <- softplus(delta + delta_bias[d]) as it is read
+  const float *delta_bias;   // (d_inner) or null; only with delta_softplus
 };
 
 // Validated arguments in, kernels enqueued on `stream` out.

@@ -31,6 +31,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "../../include/ssmscan.h"
 #include "internal.h"
 #include "s6_internal.h"
@@ -128,6 +130,36 @@ __device__ __forceinline__ size_t sum_index(const Geometry &g, int b, int c, int
 }
 
 constexpr int kPrefetch = 8;  // steps of u/delta (and y) kept in flight per lane
+constexpr float kLn2 = 0.6931471805599453f;
+
+// log(1 + e^x) = max(x, 0) + log(1 + e^-|x|): v_log_f32 on 1 + e^-|x|, or,
+// where e^-|x| < 2^-6 and 1 + e^-|x| would round much of it away, the series
+// e - e^2/2 + e^3/3 - e^4/4 (truncation below 2^-30 relative).
+__device__ __forceinline__ float softplus_f(float x) {
+  const float e = exp2_hw(-fabsf(x) * kLog2e);
+  const float l = e < 0.015625f
+                      ? e * (1.0f - e * (0.5f - e * (0.33333334f - 0.25f * e)))
+                      : __builtin_amdgcn_logf(1.0f + e) * kLn2;
+  return fmaxf(x, 0.0f) + l;
+}
+
+// What the scan does with each delta it reads: use it as given, or replace it
+// by softplus(delta + bias[d]) (the transcript's delta = softplus(projection +
+// bias), fused so that the activated delta never goes through memory).
+struct DeltaAsIs {
+  __device__ __forceinline__ float operator()(float x) const { return x; }
+};
+struct DeltaSoftplus {
+  float bias;
+  __device__ __forceinline__ float operator()(float x) const { return softplus_f(x + bias); }
+};
+template <class DX>
+__device__ __forceinline__ DX make_dx(const float *bias, int d) {
+  if constexpr (std::is_same<DX, DeltaSoftplus>::value)
+    return DeltaSoftplus{bias ? bias[d] : 0.0f};
+  else
+    return DX{};
+}
 
 // One step of the chunk-local recurrence for one lane: returns y's value.
 template <typename T, int NT>
@@ -156,12 +188,12 @@ __device__ __forceinline__ float s6_step(float dt, float x, const Row<T, NT> &Br
 // each lane's words for the next block are loaded while the current block
 // computes; B[t] and C[t] are wave-uniform scalar loads. A tail of fewer than
 // kPrefetch steps runs one step at a time.
-template <typename T, int NT, bool Reverse, bool Accumulate>
+template <typename T, int NT, bool Reverse, bool Accumulate, class DX>
 __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__restrict__ delta,
                                             const T *__restrict__ B, const T *__restrict__ C,
                                             float *__restrict__ y, const float (&Ap)[NT],
-                                            float Dd, const Geometry &g, int b, int d, int t0,
-                                            int t1, float (&h)[NT], float &S) {
+                                            float Dd, const DX &dx, const Geometry &g, int b,
+                                            int d, int t0, int t1, float (&h)[NT], float &S) {
 #pragma unroll
   for (int n = 0; n < NT; ++n) h[n] = 0.0f;
   S = 0.0f;
@@ -186,7 +218,7 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
     float cd[kPrefetch], cx[kPrefetch], cy[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      cd[j] = rd[j];
+      cd[j] = dx(rd[j]);  // transformed when used: its load has had a block of steps to land
       cx[j] = rx[j];
       if (Accumulate) cy[j] = ry[j];
     }
@@ -222,7 +254,7 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
   }
   for (int i = full; i < len; ++i) {
     const size_t r = row(i);
-    const float dt = ldv(&at(delta + r, io));
+    const float dt = dx(ldv(&at(delta + r, io)));
     const float x = ldv(&at(u + r, io));
     const int t = tof(i);
     Row<T, NT> Bc, Cc;
@@ -235,9 +267,10 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
   }
 }
 
-template <typename T, int NT>
+template <typename T, int NT, class DX>
 __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
-    const T *__restrict__ u, const T *__restrict__ delta, const float *__restrict__ A,
+    const T *__restrict__ u, const T *__restrict__ delta, const float *__restrict__ dbias,
+    const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
     float *__restrict__ y, float *__restrict__ agg_s, float *__restrict__ agg_f,
     float *__restrict__ agg_r, Geometry g, int direction) {
@@ -250,11 +283,12 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
 #pragma unroll
   for (int n = 0; n < NT; ++n) Ap[n] = A[size_t(d) * NT + n] * kLog2e;
   const float Dd = D[d];
+  const DX dx = make_dx<DX>(dbias, d);
   float h[NT];
   float S = 0.0f;
   const bool multi = g.nchunks > 1;
   if (direction != SSM_DIR_REV) {
-    chunk_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1, h, S);
+    chunk_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, h, S);
     if (multi) {
       agg_s[sum_index(g, b, c, d)] = S;
 #pragma unroll
@@ -263,9 +297,9 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
   }
   if (direction != SSM_DIR_FWD) {
     if (direction == SSM_DIR_BIDIR)
-      chunk_sweep<T, NT, true, true>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1, h, S);
+      chunk_sweep<T, NT, true, true>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, h, S);
     else
-      chunk_sweep<T, NT, true, false>(u, delta, B, C, y, Ap, Dd, g, b, d, t0, t1, h, S);
+      chunk_sweep<T, NT, true, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, h, S);
     if (multi) {
       if (direction == SSM_DIR_REV) agg_s[sum_index(g, b, c, d)] = S;
 #pragma unroll
@@ -357,11 +391,11 @@ __device__ __forceinline__ float fix_step(float S, const Row<T, NT> &Cr, const f
   return acc0 + acc1;
 }
 
-template <typename T, int NT, bool Reverse>
+template <typename T, int NT, bool Reverse, class DX>
 __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *__restrict__ C,
                                           float *__restrict__ y, const float (&Ap)[NT],
-                                          const float (&cin)[NT], const Geometry &g, int b,
-                                          int d, int t0, int t1) {
+                                          const float (&cin)[NT], const DX &dx,
+                                          const Geometry &g, int b, int d, int t0, int t1) {
   const size_t row0 = size_t(b) * g.L;
   const int len = t1 - t0;
   const int full = len - len % kPrefetch;
@@ -382,7 +416,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
     float cd[kPrefetch], cy[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      cd[j] = rd[j];
+      cd[j] = dx(rd[j]);  // transformed when used: its load has had a block of steps to land
       cy[j] = ry[j];
     }
     if (i0 + kPrefetch < full) {
@@ -406,7 +440,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   }
   for (int i = full; i < len; ++i) {
     const size_t r = row(i);
-    S += ldv(&at(delta + r, io));
+    S += dx(ldv(&at(delta + r, io)));
     Row<T, NT> Cc;
     Cc.load(C + (row0 + tof(i)) * NT);
     float &yr = at(y + r, yo);
@@ -414,9 +448,10 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   }
 }
 
-template <typename T, int NT>
+template <typename T, int NT, class DX>
 __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
-    const T *__restrict__ delta, const float *__restrict__ A, const T *__restrict__ C,
+    const T *__restrict__ delta, const float *__restrict__ dbias, const float *__restrict__ A,
+    const T *__restrict__ C,
     float *__restrict__ y, const float *__restrict__ carry_f,
     const float *__restrict__ carry_r, Geometry g, int direction) {
   int b, c, d;
@@ -430,15 +465,16 @@ __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
   float Ap[NT], cin[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) Ap[n] = A[size_t(d) * NT + n] * kLog2e;
+  const DX dx = make_dx<DX>(dbias, d);
   if (do_f) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) cin[n] = carry_f[agg_index(g, NT, b, c, n, d)];
-    fix_sweep<T, NT, false>(delta, C, y, Ap, cin, g, b, d, t0, t1);
+    fix_sweep<T, NT, false>(delta, C, y, Ap, cin, dx, g, b, d, t0, t1);
   }
   if (do_r) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) cin[n] = carry_r[agg_index(g, NT, b, c, n, d)];
-    fix_sweep<T, NT, true>(delta, C, y, Ap, cin, g, b, d, t0, t1);
+    fix_sweep<T, NT, true>(delta, C, y, Ap, cin, dx, g, b, d, t0, t1);
   }
 }
 
@@ -464,14 +500,14 @@ int plan_chunk(int batch, int L, int groups, int resident_wgs) {
 }
 
 // Workgroups of the chunk kernel resident on the whole device at once.
-template <typename T, int NT>
+template <typename T, int NT, class DX>
 int resident_chunk_wgs() {
   static int cached = 0;
   if (cached > 0) return cached;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, s6_chunk_kernel<T, NT>, kThreads,
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, s6_chunk_kernel<T, NT, DX>, kThreads,
                                                    0) != hipSuccess ||
       cus <= 0 || per_cu <= 0)
     return 1024;
@@ -479,14 +515,14 @@ int resident_chunk_wgs() {
   return cached;
 }
 
-template <typename T, int NT>
+template <typename T, int NT, class DX>
 int launch_all(const S6Args &a, hipStream_t stream) {
   Geometry g;
   g.batch = a.batch;
   g.L = a.L;
   g.d_inner = a.d_inner;
   g.groups = (a.d_inner + kThreads - 1) / kThreads;
-  g.chunk = plan_chunk(a.batch, a.L, g.groups, resident_chunk_wgs<T, NT>());
+  g.chunk = plan_chunk(a.batch, a.L, g.groups, resident_chunk_wgs<T, NT, DX>());
   g.nchunks = (a.L + g.chunk - 1) / g.chunk;
   const int64_t wgs = int64_t(g.groups) * g.nchunks * a.batch;
   if (wgs > (int64_t(1) << 31) - 1) return fail(SSM_ERR_UNSUPPORTED, "problem too large");
@@ -513,8 +549,9 @@ int launch_all(const S6Args &a, hipStream_t stream) {
   const T *dl = static_cast<const T *>(a.delta);
   const T *B = static_cast<const T *>(a.B);
   const T *C = static_cast<const T *>(a.C);
-  hipLaunchKernelGGL((s6_chunk_kernel<T, NT>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
-                     u, dl, a.A, B, C, a.D, a.y, agg_s, agg_f, agg_r, g, a.direction);
+  hipLaunchKernelGGL((s6_chunk_kernel<T, NT, DX>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
+                     u, dl, a.delta_bias, a.A, B, C, a.D, a.y, agg_s, agg_f, agg_r, g,
+                     a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 chunk launch")) return rc;
   if (g.nchunks == 1) return SSM_OK;
   const int parts = (g.nchunks + kCarryPart - 1) / kCarryPart;
@@ -522,17 +559,17 @@ int launch_all(const S6Args &a, hipStream_t stream) {
   hipLaunchKernelGGL(s6_carry_kernel, dim3(unsigned(carry_blocks)), dim3(64 * parts), 0, stream,
                      agg_s, agg_f, agg_r, a.A, car_f, car_r, g, NT, a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 carry launch")) return rc;
-  hipLaunchKernelGGL((s6_fix_kernel<T, NT>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream, dl,
-                     a.A, C, a.y, car_f, car_r, g, a.direction);
+  hipLaunchKernelGGL((s6_fix_kernel<T, NT, DX>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
+                     dl, a.delta_bias, a.A, C, a.y, car_f, car_r, g, a.direction);
   return hip_check(hipGetLastError(), "s6 fix launch");
 }
 
-template <typename T>
+template <typename T, class DX>
 int dispatch_n(const S6Args &a, hipStream_t s) {
   switch (a.N) {
 #define SSM_CASE(K) \
   case K:           \
-    return launch_all<T, K>(a, s);
+    return launch_all<T, K, DX>(a, s);
     SSM_CASE(1) SSM_CASE(2) SSM_CASE(3) SSM_CASE(4) SSM_CASE(5) SSM_CASE(6) SSM_CASE(7)
     SSM_CASE(8) SSM_CASE(9) SSM_CASE(10) SSM_CASE(11) SSM_CASE(12) SSM_CASE(13)
     SSM_CASE(14) SSM_CASE(15) SSM_CASE(16)
@@ -545,7 +582,11 @@ int dispatch_n(const S6Args &a, hipStream_t s) {
 }  // namespace
 
 int run_s6(const S6Args &a, hipStream_t stream) {
-  return a.bf16 ? dispatch_n<uint16_t>(a, stream) : dispatch_n<float>(a, stream);
+  if (a.delta_softplus)
+    return a.bf16 ? dispatch_n<uint16_t, DeltaSoftplus>(a, stream)
+                  : dispatch_n<float, DeltaSoftplus>(a, stream);
+  return a.bf16 ? dispatch_n<uint16_t, DeltaAsIs>(a, stream)
+                : dispatch_n<float, DeltaAsIs>(a, stream);
 }
 
 }  // namespace ssm

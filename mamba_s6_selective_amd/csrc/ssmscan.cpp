@@ -310,7 +310,7 @@ int ssm_selective_scan_fwd(const float *u, const float *delta, const float *A,
   if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, &noop))
     return rc;
   if (noop) return SSM_OK;
-  S6Args args{u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, false};
+  S6Args args{u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, false, false, nullptr};
   return run_s6(args, static_cast<hipStream_t>(stream));
 }
 
@@ -323,7 +323,28 @@ int ssm_selective_scan_fwd_bf16(const uint16_t *u, const uint16_t *delta, const 
   if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, &noop))
     return rc;
   if (noop) return SSM_OK;
-  S6Args args{u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, true};
+  S6Args args{u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, true, false, nullptr};
+  return run_s6(args, static_cast<hipStream_t>(stream));
+}
+
+int ssm_selective_scan_fwd_ex(const void *u, const void *delta, const float *delta_bias,
+                              const float *A, const void *B, const void *C, const float *D,
+                              float *y, int batch, int L, int d_inner, int N, int direction,
+                              unsigned flags, void *stream) {
+  g_last_error.clear();
+  if (flags & ~unsigned(SSM_FLAG_BF16 | SSM_FLAG_DELTA_SOFTPLUS))
+    return fail(SSM_ERR_INVALID_ARG, "unknown flag bits");
+  const bool softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
+  if (delta_bias && !softplus)
+    return fail(SSM_ERR_INVALID_ARG, "delta_bias is only applied with SSM_FLAG_DELTA_SOFTPLUS");
+  bool noop = false;
+  if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, &noop))
+    return rc;
+  if (noop) return SSM_OK;
+  if (delta_bias && !aligned16(delta_bias))
+    return fail(SSM_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  S6Args args{u,     delta,    A, B, C, D, y, batch, L, d_inner, N, direction,
+              (flags & SSM_FLAG_BF16) != 0, softplus, delta_bias};
   return run_s6(args, static_cast<hipStream_t>(stream));
 }
 

@@ -62,6 +62,7 @@ class S6Inputs:
     B: torch.Tensor      # (batch, L, N), fp32 or bf16
     C: torch.Tensor      # (batch, L, N), fp32 or bf16
     D: torch.Tensor      # (d_inner,) fp32
+    delta_pre: torch.Tensor | None = None  # delta's pre-activation x, storage dtype
 
     def as_f64(self):
         """The same values widened to float64 (exact for fp32 and bf16)."""
@@ -76,7 +77,8 @@ def s6_inputs(batch: int, L: int, d_inner: int, N: int, seed: int,
     Draw order: u, the pre-activation of delta, B, C (all standard normal;
     delta's pre-activation is then scaled to std 0.5 and shifted to mean -1).
     delta = log1p(exp(x)) is evaluated in float64 and rounded once to the
-    storage dtype.
+    storage dtype; x itself, rounded to the storage dtype, is kept as
+    delta_pre (the input of the scan's fused-softplus form).
     """
     if dtype not in ("f32", "bf16"):
         raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
@@ -92,7 +94,7 @@ def s6_inputs(batch: int, L: int, d_inner: int, N: int, seed: int,
     D = torch.ones(d_inner, dtype=torch.float32)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     return S6Inputs(u=u.to(tdt), delta=delta.to(tdt), A=A, B=B.to(tdt),
-                    C=C.to(tdt), D=D)
+                    C=C.to(tdt), D=D, delta_pre=x.to(tdt))
 
 
 def s6_workload_inputs(name: str) -> S6Inputs:

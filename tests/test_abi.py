@@ -118,3 +118,21 @@ def test_linear_scan_batched_argument_errors():
     assert f(FAKE_MISALIGNED, FAKE, None, FAKE, None, 2, 3, None) == ssm.SSM_ERR_INVALID_ARG
     assert f(FAKE, FAKE, None, FAKE, None, 1 << 20, (1 << 11) + 1, None) == \
         ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_selective_scan_ex_argument_errors():
+    lib = ssm.load_library()
+    f = lib.ssm_selective_scan_fwd_ex
+    args = [FAKE] * 8
+    assert f(*args, 1, 8, 4, 16, 0, 4, None) == ssm.SSM_ERR_INVALID_ARG   # unknown flag
+    assert b"flag" in lib.ssm_last_error()
+    assert f(*args, 1, 8, 4, 16, 0, 0, None) == ssm.SSM_ERR_INVALID_ARG   # bias w/o softplus
+    assert b"delta_bias" in lib.ssm_last_error()
+    no_bias = [FAKE, FAKE, None] + [FAKE] * 5
+    assert f(*no_bias, 1, 8, 4, 17, 0, ssm.SSM_FLAG_DELTA_SOFTPLUS, None) == \
+        ssm.SSM_ERR_UNSUPPORTED
+    assert f(*no_bias, 1, 8, 4, 16, 3, ssm.SSM_FLAG_DELTA_SOFTPLUS, None) == \
+        ssm.SSM_ERR_INVALID_ARG
+    assert f(*no_bias, 0, 8, 4, 16, 0, ssm.SSM_FLAG_DELTA_SOFTPLUS, None) == ssm.SSM_OK
+    mis = [FAKE, FAKE, FAKE_MISALIGNED] + [FAKE] * 5
+    assert f(*mis, 1, 8, 4, 16, 0, ssm.SSM_FLAG_DELTA_SOFTPLUS, None) == ssm.SSM_ERR_INVALID_ARG

@@ -121,3 +121,56 @@ def test_s6_zero_B_gives_skip_only():
     y = gpu_s6(inp, "bidir")
     du = (inp.u * inp.D).numpy()
     assert np.array_equal(y, du + du)
+
+
+# ---- softplus on delta fused into the scan ---------------------------------
+
+FUSED = [
+    # batch, L, d_inner, N, dtype, direction, bias
+    (2, 300, 64, 16, "f32", "fwd", True),
+    (1, 4099, 256, 8, "f32", "rev", False),
+    (3, 2048, 128, 16, "f32", "bidir", True),
+    (2, 1000, 257, 16, "bf16", "bidir", True),
+    (1, 20000, 64, 4, "bf16", "fwd", False),
+]
+
+
+def gpu_s6_fused(inp, raw, bias, direction):
+    dev = need_gpu()
+    t = [x.to(dev) for x in (inp.u, raw, inp.A, inp.B, inp.C, inp.D)]
+    y = ssm.selective_scan_fwd(*t, direction=direction, delta_softplus=True,
+                               delta_bias=None if bias is None else bias.to(dev))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[f"b{c[0]}_L{c[1]}_d{c[2]}_N{c[3]}_{c[4]}_{c[5]}"
+                                             f"{'_bias' if c[6] else ''}" for c in FUSED])
+def test_s6_fused_softplus(case):
+    """delta given before its activation, softplus(delta + bias) applied in
+    the scan. The pre-activation is widened to about +-15 so that both ways
+    the kernel evaluates log(1 + e^-|x|) run."""
+    batch, L, d, N, dt, direction, with_bias = case
+    say(f"s6 fused softplus {case}")
+    inp = s6_inputs(batch, L, d, N, seed=L + d + 3, dtype=dt)
+    raw = (inp.delta_pre.float() * 6.0).to(inp.delta_pre.dtype)
+    g = torch.Generator().manual_seed(d)
+    bias = torch.randn(d, generator=g) * 2.0 if with_bias else None
+    ref = oracle.selective_scan(inp.u.double().numpy(), raw.double().numpy(), inp.A.numpy(),
+                                inp.B.double().numpy(), inp.C.double().numpy(), inp.D.numpy(),
+                                direction, delta_bias=None if bias is None else bias.numpy(),
+                                delta_softplus=True)
+    assert_close(gpu_s6_fused(inp, raw, bias, direction), ref, TOL[dt], str(case))
+
+
+def test_s6_fused_softplus_full_size():
+    """The long bf16 workload with its delta supplied as the pre-activation
+    x ~ N(-1, 0.5): softplus fused into the scan, against the C oracle run on
+    the float64 softplus of the same values."""
+    name = "s6-fwd-b1-L65536-d1024-N16-bf16"
+    say(f"{name} fused softplus, full size")
+    inp = s6_workload_inputs(name)
+    y = gpu_s6_fused(inp, inp.delta_pre, None, "fwd")
+    d_eff = oracle.softplus(inp.delta_pre.double().numpy())
+    ref = native.selective_scan(inp.u, d_eff, inp.A, inp.B, inp.C, inp.D, "fwd")[0]
+    assert_close(y, ref, TOL["bf16"], name)
