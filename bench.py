@@ -42,14 +42,14 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kind, kernel_src):
+def load_traffic(kind, *kernel_srcs):
     """HBM bytes per launch from committed rocprofv3 counter summaries, or
     None if absent or taken on a different kernel source."""
     f = PROFILES / f"{kind}_traffic.json"
     if not f.exists():
         return None
     d = json.loads(f.read_text())
-    if d.get("kernel_source_sha") != source_hash(kernel_src):
+    if d.get("kernel_source_sha") != source_hash(*kernel_srcs):
         return None
     return d.get("bytes_per_launch")
 
@@ -283,7 +283,7 @@ def main():
     achieved = alg_bytes / (ms_kernel * 1e-3) / 1e9
     log(f"linear scan: {ms_kernel * 1e3:.1f} us/launch (min {ms_min * 1e3:.1f}), "
         f"{achieved:.0f} GB/s algorithmic")
-    traffic = load_traffic("linear_scan", "linear_scan.hip")
+    traffic = load_traffic("linear_scan", "linear_scan.hip", "scan_common.h")
     record = {
         "metric": "scan elements/s + achieved HBM GB/s (% of MI355X peak), linear & S6 fwd",
         "value": n / (ms_step * 1e-3),

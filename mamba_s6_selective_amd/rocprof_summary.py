@@ -8,7 +8,8 @@
 
     python -m mamba_s6_selective_amd.rocprof_summary traffic \\
         --fetch FETCH_results.db --write WRITE_results.db \\
-        --kernel linear_scan_kernel --copy-bytes 1073741824 --source linear_scan.hip \\
+        --kernel linear_scan_kernel --copy-bytes 1073741824 \\
+        --source linear_scan.hip scan_common.h \\
         --out profiles/linear_scan_traffic.json
         HBM bytes per launch of a kernel from two counter runs (FETCH_SIZE, then
         WRITE_SIZE, both in KiB per dispatch), each scaled by the ratio of the
@@ -107,7 +108,7 @@ def cmd_traffic(args):
         "copy_fetch_kib": cf, "copy_write_kib": cw,
         "fetch_scale": f_scale, "write_scale": w_scale,
         "bytes_per_launch": kf * 1024.0 * f_scale + kw * 1024.0 * w_scale,
-        "kernel_source_sha": source_sha(args.source),
+        "kernel_source_sha": source_sha(*args.source),
     }
     text = json.dumps(rec, indent=1)
     if args.out:
@@ -128,7 +129,8 @@ def main(argv=None):
     t.add_argument("--write", required=True)
     t.add_argument("--kernel", required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
-    t.add_argument("--source", required=True)
+    t.add_argument("--source", required=True, nargs="+",
+                   help="csrc files the kernel is built from (hashed in this order)")
     t.add_argument("--out")
     args = ap.parse_args(argv)
     {"stats": cmd_stats, "counters": cmd_counters, "traffic": cmd_traffic}[args.cmd](args)
