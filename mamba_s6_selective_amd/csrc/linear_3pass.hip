@@ -126,8 +126,11 @@ __global__ __launch_bounds__(kThreads) void local_kernel(const float *__restrict
 
 // One workgroup: thread i folds tiles [i*per, (i+1)*per), the threads'
 // totals are scanned (wave DPP scans, then the waves' totals in LDS), and each
-// thread re-walks its tiles writing the value of h entering each.
+// thread re-walks its tiles writing the value of h entering each. A thread's
+// aggregates are read kBatch at a time into registers, so that their loads
+// are in flight together and the re-walk reads no memory.
 constexpr int kCarryThreads = 1024;
+constexpr int kBatch = 16;
 
 __global__ __launch_bounds__(kCarryThreads) void carry_kernel(const float *__restrict__ agg,
                                                               float *__restrict__ hin,
@@ -137,10 +140,19 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(const float *__res
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t t0 = int64_t(threadIdx.x) * per;
+  const bool cached = per <= kBatch;  // same for every thread
+  float ra[kBatch], rb[kBatch];
   float ta = 1.0f, tb = 0.0f;
-  for (int64_t k = 0; k < per; ++k) {
-    const int64_t t = t0 + k;
-    if (t < ntiles) compose(ta, tb, agg[2 * t], agg[2 * t + 1], ta, tb);
+  for (int64_t k0 = 0; k0 < per; k0 += kBatch) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t t = t0 + k0 + j;
+      const bool in = k0 + j < per && t < ntiles;  // past the end: the identity
+      ra[j] = in ? agg[2 * t] : 1.0f;
+      rb[j] = in ? agg[2 * t + 1] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) compose(ta, tb, ra[j], rb[j], ta, tb);
   }
   float ia = ta, ib = tb;
   wave_scan(ia, ib);
@@ -156,11 +168,20 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(const float *__res
   float pa, pb;
   compose(wa, wb, xa, xb, pa, pb);
   float h = __builtin_fmaf(pa, h0, pb);
-  for (int64_t k = 0; k < per; ++k) {
-    const int64_t t = t0 + k;
-    if (t < ntiles) {
-      hin[t] = h;
-      h = __builtin_fmaf(agg[2 * t], h, agg[2 * t + 1]);
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t t = t0 + j;
+      if (j < per && t < ntiles) hin[t] = h;
+      h = __builtin_fmaf(ra[j], h, rb[j]);
+    }
+  } else {
+    for (int64_t k = 0; k < per; ++k) {
+      const int64_t t = t0 + k;
+      if (t < ntiles) {
+        hin[t] = h;
+        h = __builtin_fmaf(agg[2 * t], h, agg[2 * t + 1]);
+      }
     }
   }
 }
