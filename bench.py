@@ -109,8 +109,12 @@ def bench_linear_3pass(dev, steps, warmup, ms_single):
     a, b = a.to(dev), b.to(dev)
     h = torch.empty_like(a)
     _, ms_kernel, _ = time_steps(lambda: ssm.linear_scan_3pass(a, b, 0.0, out=h), steps, warmup)
+    # the same three passes with a register-resident Hillis-Steele local pass
+    _, ms_hs, _ = time_steps(lambda: ssm.linear_scan_hs(a, b, 0.0, out=h), steps, warmup)
     return {
         "workload": LINEAR_WORKLOAD, "ms_per_launch": round(ms_kernel, 4),
+        "hillis_steele_ms_per_launch": round(ms_hs, 4),
+        "hillis_steele_ratio": round(ms_hs / ms_kernel, 3),
         "bytes_per_elem": 28, "single_pass_bytes_per_elem": LINEAR_BYTES_PER_ELEM,
         "achieved_GBs": round(28 * n / (ms_kernel * 1e-3) / 1e9, 1),
         "predicted_ratio": round(28 / LINEAR_BYTES_PER_ELEM, 3),

@@ -100,6 +100,20 @@ int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, in
                           void *stream);
 
 /*
+ * The same recurrence and arguments, by the three-pass structure above with
+ * its local pass done as a register-resident Hillis-Steele scan: every row of
+ * 256 elements held in registers is scanned in log2(256) = 8 steps in which
+ * each element composes with the one d places back (d = 1, 2, ..., 128), with
+ * neighbouring lanes' values exchanged through cross-lane shuffles. This is
+ * the kernel form of the Hillis-Steele scan that "Selective-scan CUDA kernels"
+ * measured only in PyTorch (its introduction: the comparison "is not a fair
+ * one yet"). Same traffic as ssm_linear_scan_3pass; deterministic.
+ * Errors: as ssm_linear_scan_3pass.
+ */
+int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *h, int64_t n,
+                       void *stream);
+
+/*
  * S6 selective scan, forward / reverse / bidirectional, fp32 inputs.
  *
  * Defined by the POPCORNBENCH transcript FW-GLM-5-1 (level 2, problem 30),

@@ -28,6 +28,7 @@ _P = ctypes.c_void_p
 SIGNATURES = {
     "ssm_linear_scan": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
     "ssm_linear_scan_3pass": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
+    "ssm_linear_scan_hs": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
     "ssm_linear_scan_batched": (ctypes.c_int, [_P] * 5 + [ctypes.c_int64, ctypes.c_int64, _P]),
     "ssm_selective_scan_fwd": (ctypes.c_int, [_P] * 7 + [ctypes.c_int] * 5 + [_P]),
     "ssm_selective_scan_fwd_bf16": (ctypes.c_int, [_P] * 7 + [ctypes.c_int] * 5 + [_P]),
@@ -147,6 +148,18 @@ def linear_scan_3pass(a, b, h0: float = 0.0, out=None):
     with torch.cuda.device(a.device):
         _check(lib.ssm_linear_scan_3pass(a.data_ptr(), b.data_ptr(), float(h0),
                                          out.data_ptr(), a.numel(), _stream(a)))
+    return out
+
+
+def linear_scan_hs(a, b, h0: float = 0.0, out=None):
+    """The same recurrence, three passes with a register-resident
+    Hillis-Steele local pass."""
+    import torch
+    lib = load_library()
+    out = _linear_args(a, b, out)
+    with torch.cuda.device(a.device):
+        _check(lib.ssm_linear_scan_hs(a.data_ptr(), b.data_ptr(), float(h0),
+                                      out.data_ptr(), a.numel(), _stream(a)))
     return out
 
 

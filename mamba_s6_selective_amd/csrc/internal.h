@@ -64,8 +64,10 @@ int64_t linear3_tile_elems();
 // Device workspace the three-pass scan needs for n elements.
 size_t linear3_workspace_bytes(int64_t n);
 // Enqueues the local, carry and apply passes; `workspace` holds at least
-// linear3_workspace_bytes(n) bytes, 256-byte aligned.
+// linear3_workspace_bytes(n) bytes, 256-byte aligned. hillis_steele selects
+// the register-resident Hillis-Steele local pass.
 hipError_t launch_linear_scan_3pass(const float *a, const float *b, float h0, float *h,
-                                    int64_t n, void *workspace, hipStream_t stream);
+                                    int64_t n, void *workspace, bool hillis_steele,
+                                    hipStream_t stream);
 
 }  // namespace ssm

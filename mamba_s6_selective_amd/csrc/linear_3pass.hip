@@ -124,6 +124,125 @@ __global__ __launch_bounds__(kThreads) void local_kernel(const float *__restrict
   }
 }
 
+// Local pass by a register-resident Hillis-Steele scan ("Selective-scan CUDA
+// kernels" measured Hillis-Steele only as a PyTorch version and called the
+// comparison with its kernels not yet fair for that reason). Each row of 256
+// elements (64 lanes x 4 in registers) is scanned in log2(256) = 8 steps; in
+// the step of distance d every element e >= d becomes old[e-d] (+) old[e],
+// all reads taking the values from before the step: O(n log n) compositions
+// instead of the work-efficient pass's O(n). Neighbouring lanes' values come
+// through cross-lane shuffles. Rows, waves and the tile then combine as in
+// local_kernel, and the output is the same (A, B) per element.
+__device__ __forceinline__ float shfl_up_f(float v, int s) { return __shfl_up(v, s); }
+
+__device__ __forceinline__ void hs_row(float (&A)[4], float (&B)[4], int lane) {
+  float nA[4], nB[4];
+  {  // d = 1: element 4l+j reads 4l+j-1; item 0 reads the previous lane's item 3
+    const float pa = shfl_up_f(A[3], 1), pb = shfl_up_f(B[3], 1);
+    if (lane >= 1) compose(pa, pb, A[0], B[0], nA[0], nB[0]); else { nA[0] = A[0]; nB[0] = B[0]; }
+#pragma unroll
+    for (int j = 1; j < 4; ++j) compose(A[j - 1], B[j - 1], A[j], B[j], nA[j], nB[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { A[j] = nA[j]; B[j] = nB[j]; }
+  }
+  {  // d = 2: items 0, 1 read the previous lane's items 2, 3
+    const float pa2 = shfl_up_f(A[2], 1), pb2 = shfl_up_f(B[2], 1);
+    const float pa3 = shfl_up_f(A[3], 1), pb3 = shfl_up_f(B[3], 1);
+    if (lane >= 1) {
+      compose(pa2, pb2, A[0], B[0], nA[0], nB[0]);
+      compose(pa3, pb3, A[1], B[1], nA[1], nB[1]);
+    } else {
+      nA[0] = A[0]; nB[0] = B[0]; nA[1] = A[1]; nB[1] = B[1];
+    }
+    compose(A[0], B[0], A[2], B[2], nA[2], nB[2]);
+    compose(A[1], B[1], A[3], B[3], nA[3], nB[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { A[j] = nA[j]; B[j] = nB[j]; }
+  }
+#pragma unroll
+  for (int s = 1; s < 64; s *= 2) {  // d = 4s: the same item s lanes back
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pa = shfl_up_f(A[j], s), pb = shfl_up_f(B[j], s);
+      if (lane >= s) compose(pa, pb, A[j], B[j], nA[j], nB[j]); else { nA[j] = A[j]; nB[j] = B[j]; }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { A[j] = nA[j]; B[j] = nB[j]; }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void local_hs_kernel(const float *__restrict__ a,
+                                                            const float *__restrict__ b,
+                                                            float *__restrict__ pa,
+                                                            float *__restrict__ pb,
+                                                            float *__restrict__ agg, int64_t n) {
+  __shared__ float s_wa[kWaves], s_wb[kWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t tile = blockIdx.x;
+  const int64_t wave_start = tile * kTileElems + int64_t(wave) * kWaveElems;
+  const bool full = (tile + 1) * kTileElems <= n;
+  float A[kRows][4], B[kRows][4];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int64_t off = wave_start + r * kRowElems + lane * 4;
+    if (full) {
+      const float4 x = load_nt(a + off), y = load_nt(b + off);
+      A[r][0] = x.x; A[r][1] = x.y; A[r][2] = x.z; A[r][3] = x.w;
+      B[r][0] = y.x; B[r][1] = y.y; B[r][2] = y.z; B[r][3] = y.w;
+    } else {  // past n: the identity map (1, 0)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = off + j < n;
+        A[r][j] = in ? a[off + j] : 1.0f;
+        B[r][j] = in ? b[off + j] : 0.0f;
+      }
+    }
+  }
+  float ea[kRows], eb[kRows];  // composition of the wave's rows before row r
+  float ra = 1.0f, rb = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    hs_row(A[r], B[r], lane);
+    ea[r] = ra;
+    eb[r] = rb;
+    compose(ra, rb, lane_f(A[r][3], 63), lane_f(B[r][3], 63), ra, rb);
+  }
+  if (lane == 0) {
+    s_wa[wave] = ra;
+    s_wb[wave] = rb;
+  }
+  __syncthreads();
+  float wa = 1.0f, wb = 0.0f;  // composition of the tile's earlier waves
+  for (int w = 0; w < wave; ++w) compose(wa, wb, s_wa[w], s_wb[w], wa, wb);
+  if (wave == kWaves - 1 && lane == 0) {
+    float ta, tb;
+    compose(wa, wb, ra, rb, ta, tb);
+    agg[2 * tile] = ta;
+    agg[2 * tile + 1] = tb;
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    float qa, qb;
+    compose(wa, wb, ea[r], eb[r], qa, qb);  // everything before the row
+    float oa[4], ob[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) compose(qa, qb, A[r][j], B[r][j], oa[j], ob[j]);
+    const int64_t off = wave_start + r * kRowElems + lane * 4;
+    if (full) {
+      store_nt(pa + off, make_float4(oa[0], oa[1], oa[2], oa[3]));
+      store_nt(pb + off, make_float4(ob[0], ob[1], ob[2], ob[3]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (off + j < n) {
+          pa[off + j] = oa[j];
+          pb[off + j] = ob[j];
+        }
+    }
+  }
+}
+
 // One workgroup: thread i folds tiles [i*per, (i+1)*per), the threads'
 // totals are scanned (wave DPP scans, then the waves' totals in LDS), and each
 // thread re-walks its tiles writing the value of h entering each. A thread's
@@ -218,7 +337,8 @@ size_t linear3_workspace_bytes(int64_t n) {
 }
 
 hipError_t launch_linear_scan_3pass(const float *a, const float *b, float h0, float *h,
-                                    int64_t n, void *workspace, hipStream_t stream) {
+                                    int64_t n, void *workspace, bool hillis_steele,
+                                    hipStream_t stream) {
   const int64_t ntiles = (n + kTileElems - 1) / kTileElems;
   const auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   char *w = static_cast<char *>(workspace);
@@ -226,8 +346,12 @@ hipError_t launch_linear_scan_3pass(const float *a, const float *b, float h0, fl
   float *pb = reinterpret_cast<float *>(w + up(size_t(n) * 4));
   float *agg = reinterpret_cast<float *>(w + 2 * up(size_t(n) * 4));
   float *hin = reinterpret_cast<float *>(w + 2 * up(size_t(n) * 4) + up(size_t(ntiles) * 8));
-  hipLaunchKernelGGL(local_kernel, dim3(unsigned(ntiles)), dim3(kThreads), 0, stream, a, b, pa,
-                     pb, agg, n);
+  if (hillis_steele)
+    hipLaunchKernelGGL(local_hs_kernel, dim3(unsigned(ntiles)), dim3(kThreads), 0, stream, a, b,
+                       pa, pb, agg, n);
+  else
+    hipLaunchKernelGGL(local_kernel, dim3(unsigned(ntiles)), dim3(kThreads), 0, stream, a, b, pa,
+                       pb, agg, n);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const int64_t per = (ntiles + kCarryThreads - 1) / kCarryThreads;
   hipLaunchKernelGGL(carry_kernel, dim3(1), dim3(kCarryThreads), 0, stream, agg, hin, h0, ntiles,

@@ -251,8 +251,8 @@ int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, flo
                    "linear_scan_batched launch");
 }
 
-int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, int64_t n,
-                          void *stream) {
+static int linear_3pass_common(const float *a, const float *b, float h0, float *h, int64_t n,
+                               bool hillis_steele, void *stream) {
   g_last_error.clear();
   if (n < 0) return fail(SSM_ERR_INVALID_ARG, "n must be >= 0");
   if (n == 0) return SSM_OK;
@@ -263,7 +263,18 @@ int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   void *ws = nullptr;
   if (int rc = scratch_workspace(s, linear3_workspace_bytes(n), &ws)) return rc;
-  return hip_check(launch_linear_scan_3pass(a, b, h0, h, n, ws, s), "linear_scan_3pass launch");
+  return hip_check(launch_linear_scan_3pass(a, b, h0, h, n, ws, hillis_steele, s),
+                   "linear_scan_3pass launch");
+}
+
+int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, int64_t n,
+                          void *stream) {
+  return linear_3pass_common(a, b, h0, h, n, false, stream);
+}
+
+int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *h, int64_t n,
+                       void *stream) {
+  return linear_3pass_common(a, b, h0, h, n, true, stream);
 }
 
 int ssm_copy_f32(const float *src, float *dst, int64_t n, void *stream) {

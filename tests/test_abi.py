@@ -96,9 +96,10 @@ def test_binding_rejects_host_tensors():
         ssm.linear_scan(a, a)
 
 
-def test_linear_scan_3pass_argument_errors():
+@pytest.mark.parametrize("name", ["ssm_linear_scan_3pass", "ssm_linear_scan_hs"])
+def test_linear_scan_3pass_argument_errors(name):
     lib = ssm.load_library()
-    f = lib.ssm_linear_scan_3pass
+    f = getattr(lib, name)
     assert f(None, None, 0.0, None, 0, None) == ssm.SSM_OK
     assert f(FAKE, FAKE, 0.0, FAKE, -1, None) == ssm.SSM_ERR_INVALID_ARG
     assert f(FAKE, None, 0.0, FAKE, 5, None) == ssm.SSM_ERR_INVALID_ARG

@@ -1,4 +1,5 @@
-"""GPU parity of the three-pass linear scan against the float64 oracle.
+"""GPU parity of the three-pass linear scan (work-efficient and Hillis-Steele
+local passes) against the float64 oracle.
 
 Same bar as the single-pass scan: max |err| <= 1e-4 * (1 + |ref|) for fp32,
 bitwise identical from run to run.
@@ -18,23 +19,28 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-4
 
 
-def run3(a, b, h0=0.0):
+KINDS = {"3pass": lambda *a, **k: ssm.linear_scan_3pass(*a, **k),
+         "hs": lambda *a, **k: ssm.linear_scan_hs(*a, **k)}
+
+
+def run3(a, b, h0=0.0, kind="3pass"):
     dev = need_gpu()
-    h = ssm.linear_scan_3pass(a.to(dev), b.to(dev), h0)
+    h = KINDS[kind](a.to(dev), b.to(dev), h0)
     torch.cuda.synchronize()
     return h.cpu()
 
 
+@pytest.mark.parametrize("kind", sorted(KINDS))
 @pytest.mark.parametrize("n", EDGE_N)
-def test_3pass_edge_sizes(n):
-    say(f"3-pass edge n={n}")
+def test_3pass_edge_sizes(n, kind):
+    say(f"{kind} edge n={n}")
     a, b = linear_inputs(n, seed=900 + n, a_lo=0.5, a_hi=1.0)
     h0 = -1.25
     if n > 1_000_000:
         ref = native.linear_scan(a.numpy(), b.numpy(), h0)
     else:
         ref = oracle.linear_scan(a.numpy(), b.numpy(), h0)
-    assert_close(run3(a, b, h0).numpy(), ref, TOL, f"n={n}")
+    assert_close(run3(a, b, h0, kind).numpy(), ref, TOL, f"{kind} n={n}")
 
 
 def test_3pass_zero_length_is_noop():
@@ -43,20 +49,37 @@ def test_3pass_zero_length_is_noop():
     assert ssm.linear_scan_3pass(a, a, 1.0).numel() == 0
 
 
-def test_3pass_prefix_sum_exact():
-    say("3-pass a=1 integer prefix sum, exact")
+@pytest.mark.parametrize("kind", sorted(KINDS))
+def test_3pass_prefix_sum_exact(kind):
+    say(f"{kind} a=1 integer prefix sum, exact")
     n = 3 * 1024 * 1024 + 5
     g = torch.Generator().manual_seed(15)
     b = torch.randint(-8, 9, (n,), generator=g).float()
     a = torch.ones(n)
     ref = -2.0 + np.cumsum(b.numpy().astype(np.float64))
-    assert np.array_equal(run3(a, b, -2.0).numpy().astype(np.float64), ref)
+    assert np.array_equal(run3(a, b, -2.0, kind).numpy().astype(np.float64), ref)
 
 
-def test_3pass_signed_coefficients():
+@pytest.mark.parametrize("kind", sorted(KINDS))
+def test_3pass_signed_coefficients(kind):
     a, b = linear_inputs(300001, seed=78, a_lo=-1.0, a_hi=1.0)
     ref = oracle.linear_scan(a.numpy(), b.numpy(), 2.0)
-    assert_close(run3(a, b, 2.0).numpy(), ref, TOL, "signed")
+    assert_close(run3(a, b, 2.0, kind).numpy(), ref, TOL, f"{kind} signed")
+
+
+def test_hs_full_size_workload_and_determinism():
+    say("linear-n134217728 Hillis-Steele three-pass vs C oracle, 5 repeated runs")
+    dev = need_gpu()
+    a, b = linear_workload_inputs("linear-n134217728")
+    ad, bd = a.to(dev), b.to(dev)
+    first = ssm.linear_scan_hs(ad, bd, 0.0)
+    out = torch.empty_like(first)
+    for _ in range(4):
+        ssm.linear_scan_hs(ad, bd, 0.0, out=out)
+        assert torch.equal(out.view(torch.int32), first.view(torch.int32))
+    torch.cuda.synchronize()
+    ref = native.linear_scan(a.numpy(), b.numpy(), 0.0)
+    assert_close(first.cpu().numpy(), ref, TOL, "linear-n134217728 hs")
 
 
 def test_3pass_full_size_workload_and_determinism():
