@@ -16,6 +16,11 @@
 
 #include <stdint.h>
 
+/* The library is built with hidden visibility: only these entry points are
+ * exported, so two builds loaded into one process never bind each other's
+ * internal functions. */
+#define SSM_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -57,8 +62,8 @@ typedef enum {
  * Errors: SSM_ERR_INVALID_ARG for n < 0, null or non-16-byte-aligned a, b, h
  * with n > 0; SSM_ERR_ALLOC / SSM_ERR_HIP on runtime failure.
  */
-int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t n,
-                    void *stream);
+SSM_API int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t n,
+                            void *stream);
 
 /*
  * Batched form: nseq independent sequences of `len` elements each, stored one
@@ -81,8 +86,8 @@ int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t 
  * h with work to do; SSM_ERR_UNSUPPORTED for nseq * len > 2^31; nseq == 0 or
  * len == 0 is a no-op.
  */
-int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, float *h,
-                            float *h_last, int64_t nseq, int64_t len, void *stream);
+SSM_API int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, float *h,
+                                    float *h_last, int64_t nseq, int64_t len, void *stream);
 
 /*
  * The same recurrence and arguments as ssm_linear_scan, computed by the
@@ -96,8 +101,8 @@ int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, flo
  * workspace of about 8 bytes per element, cached per (device, stream).
  * Errors: as ssm_linear_scan, and SSM_ERR_UNSUPPORTED for n > 2^31.
  */
-int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, int64_t n,
-                          void *stream);
+SSM_API int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, int64_t n,
+                                  void *stream);
 
 /*
  * The same recurrence and arguments, by the three-pass structure above with
@@ -110,8 +115,8 @@ int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, in
  * one yet"). Same traffic as ssm_linear_scan_3pass; deterministic.
  * Errors: as ssm_linear_scan_3pass.
  */
-int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *h, int64_t n,
-                       void *stream);
+SSM_API int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *h, int64_t n,
+                               void *stream);
 
 /*
  * S6 selective scan, forward / reverse / bidirectional, fp32 inputs.
@@ -140,19 +145,19 @@ int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *h, int64
  * N outside 1..16; zero batch, L or d_inner is a no-op returning SSM_OK
  * (checked after the direction and N).
  */
-int ssm_selective_scan_fwd(const float *u, const float *delta, const float *A,
-                           const float *B, const float *C, const float *D, float *y,
-                           int batch, int L, int d_inner, int N, int direction,
-                           void *stream);
+SSM_API int ssm_selective_scan_fwd(const float *u, const float *delta, const float *A,
+                                   const float *B, const float *C, const float *D, float *y,
+                                   int batch, int L, int d_inner, int N, int direction,
+                                   void *stream);
 
 /*
  * As ssm_selective_scan_fwd, with u, delta, B and C stored as bfloat16 (raw
  * uint16 bit patterns); A, D and y stay fp32 and the state is fp32.
  */
-int ssm_selective_scan_fwd_bf16(const uint16_t *u, const uint16_t *delta,
-                                const float *A, const uint16_t *B, const uint16_t *C,
-                                const float *D, float *y, int batch, int L,
-                                int d_inner, int N, int direction, void *stream);
+SSM_API int ssm_selective_scan_fwd_bf16(const uint16_t *u, const uint16_t *delta,
+                                        const float *A, const uint16_t *B, const uint16_t *C,
+                                        const float *D, float *y, int batch, int L,
+                                        int d_inner, int N, int direction, void *stream);
 
 /* Flags of ssm_selective_scan_fwd_ex. */
 enum {
@@ -178,10 +183,10 @@ enum {
  * Errors: as ssm_selective_scan_fwd; SSM_ERR_INVALID_ARG also for unknown
  * flag bits and for delta_bias without SSM_FLAG_DELTA_SOFTPLUS.
  */
-int ssm_selective_scan_fwd_ex(const void *u, const void *delta, const float *delta_bias,
-                              const float *A, const void *B, const void *C, const float *D,
-                              float *y, int batch, int L, int d_inner, int N, int direction,
-                              unsigned flags, void *stream);
+SSM_API int ssm_selective_scan_fwd_ex(const void *u, const void *delta, const float *delta_bias,
+                                      const float *A, const void *B, const void *C, const float *D,
+                                      float *y, int batch, int L, int d_inner, int N, int direction,
+                                      unsigned flags, void *stream);
 
 /*
  * Device copy dst[i] = src[i], i < n (fp32). A known-simple streaming kernel
@@ -189,17 +194,17 @@ int ssm_selective_scan_fwd_ex(const void *u, const void *delta, const float *del
  * that must reproduce its input exactly before a timing sweep counts.
  * Errors: as ssm_linear_scan.
  */
-int ssm_copy_f32(const float *src, float *dst, int64_t n, void *stream);
+SSM_API int ssm_copy_f32(const float *src, float *dst, int64_t n, void *stream);
 
 /* Static English text for a status code. */
-const char *ssm_status_string(int code);
+SSM_API const char *ssm_status_string(int code);
 
 /* Detail of the last error raised on the calling thread ("" if none). */
-const char *ssm_last_error(void);
+SSM_API const char *ssm_last_error(void);
 
 /* Frees every cached workspace after synchronising the device(s) that own
  * them. Safe to call at any time from a thread with no call in flight. */
-int ssm_release_workspace(void);
+SSM_API int ssm_release_workspace(void);
 
 #ifdef __cplusplus
 }

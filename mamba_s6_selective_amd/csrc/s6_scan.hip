@@ -376,17 +376,75 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
 }
 
 // Carry contribution at one step: sum_n C[t,n] * cin[n] * exp(A[n] * S).
-template <typename T, int NT>
+// The carry's terms decay: with A[d,n] < 0 and the running delta sum S
+// growing, cin[n] * exp(A[d,n] * S) underflows. v_exp_f32 returns exactly 0
+// below 2^-126 (and any fp32 rounding of 2^x is 0 for x < -151), so once
+// A[d,n] * S * log2(e) < kDeadArg for every lane and every step of a block,
+// the term adds exactly zero to y and is skipped. States go in groups of
+// kFixGroup; a group is skipped for a block when the check holds for all its
+// states. The check is exact: for Ap[n] <= Ag < 0 and S_j >= Smin > 0,
+// fl(Ap[n] * S_j) <= fl(Ag * Smin) because rounding is monotone.
+constexpr int kFixGroup = 4;
+constexpr float kDeadArg = -152.0f;
+
+template <int NT>
+struct FixGroups {
+  static constexpr int kCount = (NT + kFixGroup - 1) / kFixGroup;
+  float Ag[kCount];   // largest Ap[n] of the group
+  bool keep[kCount];  // never skipped: a non-finite carry, a NaN or non-negative Ap
+  __device__ __forceinline__ FixGroups(const float (&Ap)[NT], const float (&cin)[NT]) {
+#pragma unroll
+    for (int g = 0; g < kCount; ++g) {
+      float ag = -__builtin_inff();
+      bool k = false;
+#pragma unroll
+      for (int i = 0; i < kFixGroup; ++i) {
+        const int n = g * kFixGroup + i;
+        if (n < NT) {
+          ag = fmaxf(ag, Ap[n]);
+          k = k || !__builtin_isfinite(cin[n]) || Ap[n] != Ap[n];
+        }
+      }
+      Ag[g] = ag;
+      keep[g] = k || !(ag < 0.0f);
+    }
+  }
+  // Bit g set: group g has a lane whose term may be non-zero at one of the
+  // block's running sums Sj.
+  __device__ __forceinline__ uint32_t live(const float (&Sj)[kPrefetch]) const {
+    float smin = Sj[0];
+#pragma unroll
+    for (int j = 1; j < kPrefetch; ++j) smin = fminf(smin, Sj[j]);
+    // A NaN in the sum reaches the block's last step; fminf would drop it.
+    const bool sane = Sj[kPrefetch - 1] == Sj[kPrefetch - 1];
+    uint32_t m = 0;
+#pragma unroll
+    for (int g = 0; g < kCount; ++g) {
+      const bool dead = !keep[g] && sane && Ag[g] * smin < kDeadArg;
+      if (__builtin_amdgcn_ballot_w64(!dead) != 0) m |= 1u << g;
+    }
+    return m;
+  }
+};
+
+template <typename T, int NT, bool Gated>
 __device__ __forceinline__ float fix_step(float S, const Row<T, NT> &Cr, const float (&Ap)[NT],
-                                          const float (&cin)[NT]) {
+                                          const float (&cin)[NT], uint32_t live) {
   float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const float v = cin[n] * exp2_hw(Ap[n] * S);
-    if (n & 1)
-      acc1 = __builtin_fmaf(Cr.get(n), v, acc1);
-    else
-      acc0 = __builtin_fmaf(Cr.get(n), v, acc0);
+  for (int g = 0; g < FixGroups<NT>::kCount; ++g) {
+    if (Gated && !((live >> g) & 1u)) continue;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < kFixGroup; ++i) {
+      const int n = g * kFixGroup + i;
+      if (n < NT) {
+        const float v = cin[n] * exp2_hw(Ap[n] * S);
+        if (n & 1)
+          acc1 = __builtin_fmaf(Cr.get(n), v, acc1);
+        else
+          acc0 = __builtin_fmaf(Cr.get(n), v, acc0);
+      }
+    }
   }
   return acc0 + acc1;
 }
@@ -403,6 +461,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   auto row = [&](int i) { return (row0 + tof(i)) * size_t(g.d_inner); };
   const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));
   const uint32_t yo = uint32_t(d) * 4u;
+  const FixGroups<NT> groups(Ap, cin);
   float rd[kPrefetch], ry[kPrefetch];
   if (full > 0) {
 #pragma unroll
@@ -413,10 +472,11 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   }
   float S = 0.0f;
   for (int i0 = 0; i0 < full; i0 += kPrefetch) {
-    float cd[kPrefetch], cy[kPrefetch];
+    float Sj[kPrefetch], cy[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      cd[j] = dx(rd[j]);  // transformed when used: its load has had a block of steps to land
+      S += dx(rd[j]);  // transformed when used: its load has had a block of steps to land
+      Sj[j] = S;
       cy[j] = ry[j];
     }
     if (i0 + kPrefetch < full) {
@@ -426,6 +486,8 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
         ry[j] = at(y + row(i0 + kPrefetch + j), yo);
       }
     }
+    const uint32_t live = groups.live(Sj);
+    if (live == 0) continue;  // every term of the block is exactly zero: y stays as it is
     Row<T, NT> Cc;
     Cc.load(C + (row0 + tof(i0)) * NT);
 #pragma unroll
@@ -433,8 +495,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
       Row<T, NT> Cn;
       wait_scalar_loads();
       if (j + 1 < kPrefetch) Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
-      S += cd[j];
-      at(y + row(i0 + j), yo) = cy[j] + fix_step<T, NT>(S, Cc, Ap, cin);
+      at(y + row(i0 + j), yo) = cy[j] + fix_step<T, NT, true>(Sj[j], Cc, Ap, cin, live);
       if (j + 1 < kPrefetch) Cc = Cn;
     }
   }
@@ -444,7 +505,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
     Row<T, NT> Cc;
     Cc.load(C + (row0 + tof(i)) * NT);
     float &yr = at(y + r, yo);
-    yr = yr + fix_step<T, NT>(S, Cc, Ap, cin);
+    yr = yr + fix_step<T, NT, false>(S, Cc, Ap, cin, 0);
   }
 }
 

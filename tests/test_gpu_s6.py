@@ -123,6 +123,49 @@ def test_s6_zero_B_gives_skip_only():
     assert np.array_equal(y, du + du)
 
 
+@pytest.mark.parametrize("chunk", ["256", "1024"])
+def test_s6_decayed_carry_terms(chunk, monkeypatch):
+    """The fix pass skips a group of states for a block once every lane's carry
+    term there is exactly zero. States decay at very different rates here, the
+    slow ones sit in different groups per test row, one channel keeps a group
+    alive that every other channel has let die, and one group has A > 0 (never
+    skipped); a wrongly skipped group would add an O(1) error."""
+    say(f"s6 decayed carry terms chunk={chunk}")
+    monkeypatch.setenv("SSMSCAN_S6_CHUNK", chunk)
+    inp = s6_inputs(2, 3000, 128, 16, seed=515, dtype="f32")
+    g = torch.Generator().manual_seed(5)
+    inp.delta = torch.rand(inp.delta.shape, generator=g) + 0.5
+    A = torch.empty(128, 16)
+    A[:, 0:4] = -20.0
+    A[:, 4:8] = -3.0
+    A[:, 8:12] = -0.5
+    A[:, 12:16] = -0.01
+    A[64:, :] = A[64:, :].flip(1)  # slow states in the first group for the second wave
+    A[37, 0:4] = -0.02             # one channel keeps the fastest group alive
+    A[100, 4] = 0.0005             # and one has a growing state (never skipped),
+    inp.u[:, :, 100] *= 0.01       # its input scaled so that fp32 can follow the sum
+    inp.A = A
+    for direction in ("fwd", "rev", "bidir"):
+        assert_close(gpu_s6(inp, direction), ref_s6(inp, direction), TOL["f32"], direction)
+
+
+def test_s6_decay_with_negative_delta():
+    """delta taken as given may be negative, so the running sum that decides
+    which carry terms are zero can fall within a block."""
+    say("s6 negative delta")
+    monkeypatch = pytest.MonkeyPatch()
+    monkeypatch.setenv("SSMSCAN_S6_CHUNK", "512")
+    try:
+        inp = s6_inputs(1, 2048, 64, 16, seed=616, dtype="f32")
+        g = torch.Generator().manual_seed(6)
+        inp.delta = torch.randn(inp.delta.shape, generator=g) * 0.3 + 0.25  # a fifth < 0
+        inp.A = -torch.rand(64, 16, generator=g) * 6 - 0.5
+        for direction in ("fwd", "rev"):
+            assert_close(gpu_s6(inp, direction), ref_s6(inp, direction), TOL["f32"], direction)
+    finally:
+        monkeypatch.undo()
+
+
 # ---- softplus on delta fused into the scan ---------------------------------
 
 FUSED = [
