@@ -108,6 +108,7 @@ __device__ __forceinline__ void load_row(const T *__restrict__ p, float (&out)[N
 
 struct Geometry {
   int batch, L, d_inner, groups, nchunks, chunk;
+  int full_fix;  // 1: the fix pass evaluates every carry term (no skipped groups or blocks)
 };
 
 __device__ __forceinline__ void decompose(const Geometry &g, int &b, int &c, int &d) {
@@ -377,55 +378,123 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
 
 // Carry contribution at one step: sum_n C[t,n] * cin[n] * exp(A[n] * S).
 // The carry's terms decay: with A[d,n] < 0 and the running delta sum S
-// growing, cin[n] * exp(A[d,n] * S) underflows. v_exp_f32 returns exactly 0
-// below 2^-126 (and any fp32 rounding of 2^x is 0 for x < -151), so once
-// A[d,n] * S * log2(e) < kDeadArg for every lane and every step of a block,
-// the term adds exactly zero to y and is skipped. States go in groups of
-// kFixGroup; a group is skipped for a block when the check holds for all its
-// states. The check is exact: for Ap[n] <= Ag < 0 and S_j >= Smin > 0,
-// fl(Ap[n] * S_j) <= fl(Ag * Smin) because rounding is monotone.
+// growing, cin[n] * exp(A[d,n] * S) shrinks. Two exact shortcuts follow.
+//
+// Zero terms: v_exp_f32 returns exactly 0 below 2^-126 (and any fp32
+// rounding of 2^x is 0 for x < -151), so once A[d,n] * S * log2(e) < kDeadArg
+// for every lane and every step of a block, the term adds exactly zero to y
+// and is skipped. States go in groups of kFixGroup; a group is skipped for a
+// block when this holds for all its states. For Ap[n] <= Ag < 0 and
+// S_j >= Smin > 0, fl(Ap[n] * S_j) <= fl(Ag * Smin) since rounding is monotone.
+//
+// Negligible blocks: the whole correction at step j is at most
+// maxC * sum_g (sum_{n in g} |cin[n]|) * 2^(Ag * Smin), maxC the largest |C|
+// over the chunk. When that bound, times 2^26 and a margin that covers its
+// own rounding and the hardware exp2's error, is below |y| (a normal number)
+// at every step of the block in every lane, the correction is under a
+// quarter of y's spacing and y + correction rounds to y: the block is left
+// as it is, stores included.
 constexpr int kFixGroup = 4;
 constexpr float kDeadArg = -152.0f;
+constexpr float kNegligible = 67822182.4f;  // 2^26 * 1.01
+constexpr float kTinyY = 0x1p-100f;          // smaller |y| never counts as resolving the bound
+constexpr int kNegligibleMinLen = 64;        // chunks shorter than this skip the test
 
 template <int NT>
 struct FixGroups {
   static constexpr int kCount = (NT + kFixGroup - 1) / kFixGroup;
-  float Ag[kCount];   // largest Ap[n] of the group
-  bool keep[kCount];  // never skipped: a non-finite carry, a NaN or non-negative Ap
+  float Ag[kCount];    // largest Ap[n] of the group
+  float cabs[kCount];  // sum of |cin[n]| over the group
+  bool keep[kCount];   // never skipped: a non-finite carry, a NaN or non-negative Ap
+  bool any_keep;
   __device__ __forceinline__ FixGroups(const float (&Ap)[NT], const float (&cin)[NT]) {
+    any_keep = false;
 #pragma unroll
     for (int g = 0; g < kCount; ++g) {
-      float ag = -__builtin_inff();
+      float ag = -__builtin_inff(), ca = 0.0f;
       bool k = false;
 #pragma unroll
       for (int i = 0; i < kFixGroup; ++i) {
         const int n = g * kFixGroup + i;
         if (n < NT) {
           ag = fmaxf(ag, Ap[n]);
+          ca += fabsf(cin[n]);
           k = k || !__builtin_isfinite(cin[n]) || Ap[n] != Ap[n];
         }
       }
       Ag[g] = ag;
+      cabs[g] = ca;
       keep[g] = k || !(ag < 0.0f);
+      any_keep = any_keep || keep[g];
     }
   }
-  // Bit g set: group g has a lane whose term may be non-zero at one of the
-  // block's running sums Sj.
-  __device__ __forceinline__ uint32_t live(const float (&Sj)[kPrefetch]) const {
+  // Decides what a block of kPrefetch steps with running sums Sj and current
+  // outputs cy needs. Returns 0 when the block leaves y unchanged; otherwise
+  // bit g is set when group g has a lane whose term may be non-zero.
+  // cscale = maxC * kNegligible (infinite when C holds a non-finite value,
+  // or to leave the negligible-block test out).
+  __device__ __forceinline__ uint32_t live(const float (&Sj)[kPrefetch],
+                                           const float (&cy)[kPrefetch], float cscale) const {
     float smin = Sj[0];
 #pragma unroll
     for (int j = 1; j < kPrefetch; ++j) smin = fminf(smin, Sj[j]);
     // A NaN in the sum reaches the block's last step; fminf would drop it.
     const bool sane = Sj[kPrefetch - 1] == Sj[kPrefetch - 1];
+    float p[kCount];
+#pragma unroll
+    for (int g = 0; g < kCount; ++g) p[g] = Ag[g] * smin;
+    if (cscale < __builtin_inff()) {  // wave-uniform
+      float bound = 0.0f;
+#pragma unroll
+      for (int g = 0; g < kCount; ++g) bound = fmaf(cabs[g], exp2_hw(p[g]), bound);
+      const float t = bound * cscale;
+      const float thr = (sane && !any_keep && t == t) ? fmaxf(t, kTinyY) : __builtin_inff();
+      bool resolved = true;
+#pragma unroll
+      for (int j = 0; j < kPrefetch; ++j) resolved = resolved && fabsf(cy[j]) > thr;
+      if (__builtin_amdgcn_ballot_w64(!resolved) == 0) return 0;
+    }
     uint32_t m = 0;
 #pragma unroll
     for (int g = 0; g < kCount; ++g) {
-      const bool dead = !keep[g] && sane && Ag[g] * smin < kDeadArg;
+      const bool dead = !keep[g] && sane && p[g] < kDeadArg;
       if (__builtin_amdgcn_ballot_w64(!dead) != 0) m |= 1u << g;
     }
     return m;
   }
 };
+
+// maxC * kNegligible for the chunk's C rows [first, first + count) (element
+// offsets), the same in every lane: the rows are read as words spread over
+// the wave's active lanes (a prefix of the wave) and their magnitudes, as
+// bit patterns, reduced with a wave-wide unsigned max. A NaN or infinity
+// gives +inf.
+template <typename T, int NT>
+__device__ __forceinline__ float chunk_cscale(const T *__restrict__ C, size_t first, int count) {
+  const uint32_t lane = __lane_id();
+  const uint32_t nact = uint32_t(__popcll(__builtin_amdgcn_read_exec()));
+  uint32_t m = 0;
+  if constexpr (sizeof(T) == 2 && NT % 2 == 0) {
+    // bf16 rows of even length: 32-bit words of two values each (first is even).
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(C + first);
+    const uint32_t words = uint32_t(count) / 2;
+    for (uint32_t i = lane; i < words; i += nact) {
+      const uint32_t x = w[i];
+      m = max(m, max((x << 16) & 0x7fffffffu, x & 0x7fff0000u));
+    }
+  } else {
+    for (uint32_t i = lane; i < uint32_t(count); i += nact) {
+      uint32_t x;
+      if constexpr (sizeof(T) == 2)
+        x = uint32_t(C[first + i]) << 16;
+      else
+        x = __float_as_uint(C[first + i]);
+      m = max(m, x & 0x7fffffffu);
+    }
+  }
+  m = __ockl_wfred_max_u32(m);
+  return m >= 0x7f800000u ? __builtin_inff() : __uint_as_float(m) * kNegligible;
+}
 
 template <typename T, int NT, bool Gated>
 __device__ __forceinline__ float fix_step(float S, const Row<T, NT> &Cr, const float (&Ap)[NT],
@@ -462,6 +531,10 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));
   const uint32_t yo = uint32_t(d) * 4u;
   const FixGroups<NT> groups(Ap, cin);
+  // Short chunks end before their carry has decayed far enough: no test.
+  const float cscale = (len >= kNegligibleMinLen && !g.full_fix)
+                           ? chunk_cscale<T, NT>(C, (row0 + t0) * NT, len * NT)
+                           : __builtin_inff();
   float rd[kPrefetch], ry[kPrefetch];
   if (full > 0) {
 #pragma unroll
@@ -486,8 +559,8 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
         ry[j] = at(y + row(i0 + kPrefetch + j), yo);
       }
     }
-    const uint32_t live = groups.live(Sj);
-    if (live == 0) continue;  // every term of the block is exactly zero: y stays as it is
+    const uint32_t live = g.full_fix ? ~0u : groups.live(Sj, cy, cscale);
+    if (live == 0) continue;  // the block leaves y as it is
     Row<T, NT> Cc;
     Cc.load(C + (row0 + tof(i0)) * NT);
 #pragma unroll
@@ -584,6 +657,10 @@ int launch_all(const S6Args &a, hipStream_t stream) {
   g.d_inner = a.d_inner;
   g.groups = (a.d_inner + kThreads - 1) / kThreads;
   g.chunk = plan_chunk(a.batch, a.L, g.groups, resident_chunk_wgs<T, NT, DX>());
+  // SSMSCAN_S6_FULL_FIX=1 turns the fix pass's exact shortcuts off (every
+  // carry term evaluated), so that their results can be compared bit for bit.
+  const char *full = getenv("SSMSCAN_S6_FULL_FIX");
+  g.full_fix = (full && atoi(full) != 0) ? 1 : 0;
   g.nchunks = (a.L + g.chunk - 1) / g.chunk;
   const int64_t wgs = int64_t(g.groups) * g.nchunks * a.batch;
   if (wgs > (int64_t(1) << 31) - 1) return fail(SSM_ERR_UNSUPPORTED, "problem too large");

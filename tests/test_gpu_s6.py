@@ -166,6 +166,48 @@ def test_s6_decay_with_negative_delta():
         monkeypatch.undo()
 
 
+def _s6_any(inp, direction, fused):
+    if not fused:
+        return gpu_s6(inp, direction)
+    dev = need_gpu()
+    t = [x.to(dev) for x in (inp.u, inp.delta_pre, inp.A, inp.B, inp.C, inp.D)]
+    y = ssm.selective_scan_fwd(*t, direction=direction, delta_softplus=True)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+FULL_FIX = [  # (batch, L, d_inner, dtype, chunk, fused)
+    (1, 8192, 512, "bf16", "256", False),
+    (2, 4096, 320, "f32", "1024", False),
+    (1, 6000, 256, "bf16", "512", True),
+    (4, 2048, 1536, "bf16", "160", False),
+]
+
+
+@pytest.mark.parametrize("case", FULL_FIX, ids=[f"b{c[0]}_L{c[1]}_d{c[2]}_{c[3]}_c{c[4]}"
+                                                 f"{'_fused' if c[5] else ''}" for c in FULL_FIX])
+def test_s6_fix_shortcuts_are_exact(case, monkeypatch):
+    """The fix pass's skipped carry groups and left-alone blocks change no
+    output bit: the result equals, value for value, the one with every carry
+    term evaluated. Some channels get tiny outputs (D = 0 and small u), whose
+    blocks the negligible-block test must not leave alone."""
+    b, L, d, dt, chunk, fused = case
+    say(f"s6 fix shortcuts exact {case}")
+    monkeypatch.setenv("SSMSCAN_S6_CHUNK", chunk)
+    inp = s6_inputs(b, L, d, 16, seed=L + d, dtype=dt)
+    inp.D = inp.D.clone()
+    inp.D[::7] = 0.0
+    inp.u[:, :, ::7] = (inp.u[:, :, ::7].float() * 1e-6).to(inp.u.dtype)
+    for direction in ("fwd", "rev", "bidir"):
+        monkeypatch.delenv("SSMSCAN_S6_FULL_FIX", raising=False)
+        fast = _s6_any(inp, direction, fused)
+        monkeypatch.setenv("SSMSCAN_S6_FULL_FIX", "1")
+        full = _s6_any(inp, direction, fused)
+        same = fast == full  # -0 == +0; no NaN arises here
+        say(f"  {direction}: {int((~same).sum())} of {same.size} differ")
+        assert same.all(), direction
+
+
 # ---- softplus on delta fused into the scan ---------------------------------
 
 FUSED = [
