@@ -67,10 +67,10 @@ def source_sha(*files: str) -> str:
 
 
 def cmd_stats(args):
-    print(f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'total_us':>12}")
+    print(f"{'kernel':<64} {'calls':>6} {'avg_us':>10} {'total_us':>12}")
     for db in args.dbs:
         for name, calls, total, avg in kernel_stats(db):
-            print(f"{name[:60]:<60} {calls:>6} {avg:>10.2f} {total:>12.1f}")
+            print(f"{name[:64]:<64} {calls:>6} {avg:>10.2f} {total:>12.1f}")
 
 
 def cmd_counters(args):
@@ -79,10 +79,10 @@ def cmd_counters(args):
         "select distinct counter_name from counters_collection")})
     per = {c: counter_per_dispatch(args.db, c) for c in names}
     kernels = sorted({k for d in per.values() for k in d})
-    print(f"{'kernel':<48} " + " ".join(f"{c:>24}" for c in names))
+    print(f"{'kernel':<64} " + " ".join(f"{c:>24}" for c in names))
     for k in kernels:
         vals = [statistics.median(per[c][k]) if per[c].get(k) else float("nan") for c in names]
-        print(f"{k[:48]:<48} " + " ".join(f"{v:>24.4g}" for v in vals))
+        print(f"{k[:64]:<64} " + " ".join(f"{v:>24.4g}" for v in vals))
 
 
 def pick(d, key):
