@@ -208,6 +208,28 @@ def test_s6_fix_shortcuts_are_exact(case, monkeypatch):
         assert same.all(), direction
 
 
+def test_s6_fix_shortcuts_exact_with_nonfinite(monkeypatch):
+    """Non-finite values keep the shortcuts exact: a NaN input (a NaN carry
+    from then on), an infinite C (max|C| infinite for its chunk) and an
+    infinite delta (the running sum infinite) give the same outputs, NaN for
+    NaN, with and without the shortcuts."""
+    say("s6 fix shortcuts exact with non-finite inputs")
+    monkeypatch.setenv("SSMSCAN_S6_CHUNK", "256")
+    inp = s6_inputs(2, 4096, 256, 16, seed=777, dtype="f32")
+    inp.u[0, 300, 5] = float("nan")
+    inp.C[0, 1700, 3] = float("inf")
+    inp.delta[1, 2100, 9] = float("inf")
+    inp.u[1, 3000, 200] = float("inf")
+    for direction in ("fwd", "rev", "bidir"):
+        monkeypatch.delenv("SSMSCAN_S6_FULL_FIX", raising=False)
+        fast = gpu_s6(inp, direction)
+        monkeypatch.setenv("SSMSCAN_S6_FULL_FIX", "1")
+        full = gpu_s6(inp, direction)
+        say(f"  {direction}: non-finite outputs {int((~np.isfinite(full)).sum())}")
+        assert (~np.isfinite(full)).any()
+        assert np.array_equal(fast, full, equal_nan=True), direction
+
+
 # ---- softplus on delta fused into the scan ---------------------------------
 
 FUSED = [
