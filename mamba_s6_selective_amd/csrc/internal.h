@@ -39,7 +39,7 @@ struct LinearStatus {
 constexpr int64_t kLinearMaxTiles = int64_t(64) * 64 * 64;
 
 // Elements per tile of the look-back scan.
-int64_t linear_tile_elems();
+int64_t linear_tile_elems(bool segmented);
 
 // Enqueues the single-pass scan on min(ntiles, resident_wgs) persistent
 // workgroups. The status levels must hold ntiles, ceil(ntiles/64) and

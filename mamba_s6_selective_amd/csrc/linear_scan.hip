@@ -13,7 +13,8 @@
 // L2s, where a status read that must see other XCDs' writes takes several
 // microseconds while HBM is streaming:
 //
-//  * tile = 8 data waves x 4 rows x 64 lanes x float4 = 8192 elements. Each row
+//  * tile = 8 data waves x 4 rows x 64 lanes x float4 = 8192 elements (the
+//    batched form: 11 waves x 3 rows = 8448, see Shape). Each row
 //    is read and written with one fully coalesced 1 KiB global_load/store_dwordx4
 //    per wave (no LDS transpose). Per lane: 4-element chunk aggregates in
 //    registers; per row: a wave64 inclusive scan of chunk aggregates with DPP
@@ -40,7 +41,7 @@
 //    a ticket counter, so a tile only ever waits for lower tiles that running
 //    workgroups own, and the lowest unfinished tile can always finish (no
 //    assumption about how many workgroups are resident). Each workgroup has
-//    eight data waves and one control wave, and a tile moves through a
+//    its data waves and one control wave, and a tile moves through a
 //    four-stage pipeline (load, scan and publish, look-back, apply and store)
 //    in which every long-latency step -- a tile's loads, the status reads of
 //    its look-back -- is issued one iteration before its result is used.
@@ -57,13 +58,23 @@
 namespace ssm {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kRows = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowElems = 256;                    // 64 lanes x float4
-constexpr int kWaveElems = kRowElems * kRows;     // 1024
-constexpr int kTileElems = kWaveElems * kWaves;   // 8192
-constexpr int kFan = 64;                          // entries per look-back window
+constexpr int kRowElems = 256;  // 64 lanes x float4
+constexpr int kFan = 64;        // entries per look-back window
+
+// Tile shape: data waves per workgroup and float4 rows per wave. One
+// sequence: 8 x 4 rows = 8192 elements. The batched form spends more VALU per
+// element (segment positions, the reset policy) and runs 7-11 % faster with
+// more, shorter waves, 11 x 3 rows = 8448 elements (as many waves as fit the
+// register file, with the parked tiles within LDS); for one sequence that
+// shape is no faster.
+template <bool Seg>
+struct Shape {
+  static constexpr int kWaves = Seg ? 11 : 8;
+  static constexpr int kRows = Seg ? 3 : 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWaveElems = kRowElems * kRows;
+  static constexpr int kTileElems = kWaveElems * kWaves;
+};
 
 using namespace scan;
 
@@ -265,8 +276,10 @@ __device__ __forceinline__ bool seg_edge(uint32_t i, const Segments &sg) {
 template <bool Seg>
 __device__ __forceinline__ void load_tile(const float *__restrict__ a,
                                           const float *__restrict__ b, int64_t n, int64_t tile,
-                                          const Segments &sg, float4 (&va)[kRows],
-                                          float4 (&vb)[kRows]) {
+                                          const Segments &sg, float4 (&va)[Shape<Seg>::kRows],
+                                          float4 (&vb)[Shape<Seg>::kRows]) {
+  constexpr int kRows = Shape<Seg>::kRows, kWaveElems = Shape<Seg>::kWaveElems,
+                kTileElems = Shape<Seg>::kTileElems;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t wave_start = tile * kTileElems + int64_t(wave) * kWaveElems;
@@ -319,7 +332,7 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ a,
 
 // Data waves, phase 1: chunk aggregates of the lane's 4 items per row, a wave
 // scan per row, and the wave's aggregate (rows folded in order) into LDS.
-template <class Op>
+template <class Op, int kRows>
 __device__ __forceinline__ void tile_local_scan(const float4 (&va)[kRows],
                                                 const float4 (&vb)[kRows], float (&ia)[kRows],
                                                 float (&ib)[kRows], float *s_wave_a,
@@ -351,11 +364,12 @@ __device__ __forceinline__ void tile_local_scan(const float4 (&va)[kRows],
 // Data waves, phase 2: carry into each row, then into each lane's chunk, then
 // re-run the recurrence over the lane's 4 items and store (with segments,
 // the last value of each sequence also goes to h_last).
-template <bool Seg, class Op>
+template <bool Seg, class Op, int kRows = Shape<Seg>::kRows>
 __device__ __forceinline__ void tile_apply(const float4 (&va)[kRows], const float4 (&vb)[kRows],
                                            const float (&ia)[kRows], const float (&ib)[kRows],
                                            float c, float *__restrict__ h, int64_t n,
                                            int64_t tile, const Segments &sg) {
+  constexpr int kWaveElems = Shape<Seg>::kWaveElems, kTileElems = Shape<Seg>::kTileElems;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t wave_start = tile * kTileElems + int64_t(wave) * kWaveElems;
@@ -426,7 +440,9 @@ __device__ __forceinline__ int64_t successor(int64_t t, int64_t ntiles,
 // and every hand-over crosses a barrier. The parked a/b of two tiles wait
 // there for their look-backs (slot j % 2; each wave reads back only what it
 // wrote itself).
+template <bool Seg>
 struct Shared {
+  static constexpr int kWaves = Shape<Seg>::kWaves, kRows = Shape<Seg>::kRows;
   float4 park[2][kWaves][kRows][2][64];        // a, b rows of two parked tiles
   float wave_a[4][kWaves], wave_b[4][kWaves];  // per-wave aggregates
   float tile_a[4], tile_b[4];                  // tile aggregates
@@ -435,7 +451,8 @@ struct Shared {
   unsigned arrived[2];                         // data waves done with a tile's local scan
 };
 
-__device__ __forceinline__ void park(Shared &sh, int slot, const float4 (&va)[kRows],
+template <bool Seg, int kRows = Shape<Seg>::kRows>
+__device__ __forceinline__ void park(Shared<Seg> &sh, int slot, const float4 (&va)[kRows],
                                      const float4 (&vb)[kRows]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -445,7 +462,8 @@ __device__ __forceinline__ void park(Shared &sh, int slot, const float4 (&va)[kR
     sh.park[slot][wave][r][1][lane] = vb[r];
   }
 }
-__device__ __forceinline__ void unpark(const Shared &sh, int slot, float4 (&va)[kRows],
+template <bool Seg, int kRows = Shape<Seg>::kRows>
+__device__ __forceinline__ void unpark(const Shared<Seg> &sh, int slot, float4 (&va)[kRows],
                                        float4 (&vb)[kRows]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -459,14 +477,15 @@ __device__ __forceinline__ void unpark(const Shared &sh, int slot, float4 (&va)[
 // Data waves: local scan of a loaded tile; the last data wave to finish folds
 // the wave aggregates into the tile aggregate and publishes it (level 0) at
 // once, without waiting for any other workgroup.
-template <class Op>
+template <class Op, bool Seg, int kRows = Shape<Seg>::kRows>
 __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
                                                  const float4 (&vb)[kRows], float (&ia)[kRows],
-                                                 float (&ib)[kRows], Shared &sh, int ring, int slot,
-                                                 const LinearStatus &st, int64_t tile,
+                                                 float (&ib)[kRows], Shared<Seg> &sh, int ring,
+                                                 int slot, const LinearStatus &st, int64_t tile,
                                                  uint32_t epoch) {
+  constexpr int kWaves = Shape<Seg>::kWaves;
   const int lane = threadIdx.x & 63;
-  tile_local_scan<Op>(va, vb, ia, ib, sh.wave_a[ring], sh.wave_b[ring]);
+  tile_local_scan<Op, kRows>(va, vb, ia, ib, sh.wave_a[ring], sh.wave_b[ring]);
   unsigned prior = 0;
   if (lane == 0)
     prior = __hip_atomic_fetch_add(&sh.arrived[slot], 1u, __ATOMIC_ACQ_REL,
@@ -523,12 +542,13 @@ __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
 // The ticket of a launch is st.ticket[epoch & 1]; the first workgroup zeroes
 // the other slot for the next launch on the stream.
 template <bool Seg>
-__global__ __launch_bounds__(kThreads + 64) void linear_scan_kernel(
+__global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
     const float *__restrict__ a, const float *__restrict__ b, float h0,
     float *__restrict__ h, int64_t n, int64_t ntiles, LinearStatus st, uint32_t epoch,
     Segments sg) {
   using Op = typename std::conditional<Seg, ResetOp, PlainOp>::type;
-  __shared__ Shared sh;
+  constexpr int kWaves = Shape<Seg>::kWaves, kRows = Shape<Seg>::kRows;
+  __shared__ Shared<Seg> sh;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   unsigned long long *ticket = st.ticket + (epoch & 1u);
@@ -603,7 +623,7 @@ __global__ __launch_bounds__(kThreads + 64) void linear_scan_kernel(
   if (t0 < ntiles) load_tile<Seg>(a, b, n, t0, sg, va, vb);
   if (t1 < ntiles) load_tile<Seg>(a, b, n, t1, sg, na, nb);
   if (t0 < ntiles) {
-    scan_and_publish<Op>(va, vb, iaw, ibw, sh, 0, 0, st, t0, epoch);
+    scan_and_publish<Op, Seg>(va, vb, iaw, ibw, sh, 0, 0, st, t0, epoch);
     park(sh, 0, va, vb);
   }
   __syncthreads();  // B
@@ -615,7 +635,7 @@ __global__ __launch_bounds__(kThreads + 64) void linear_scan_kernel(
     if (t2 < ntiles) load_tile<Seg>(a, b, n, t2, sg, ma, mb);
     float nia[kRows], nib[kRows];
     if (t1 < ntiles)
-      scan_and_publish<Op>(na, nb, nia, nib, sh, (j + 1) & 3, (j + 1) & 1, st, t1, epoch);
+      scan_and_publish<Op, Seg>(na, nb, nia, nib, sh, (j + 1) & 3, (j + 1) & 1, st, t1, epoch);
     if (wave == 0 && lane == 0) sh.ids[(j + 3) & 3] = claimed;
     __syncthreads();  // C_j
     if (tp < ntiles) {
@@ -651,7 +671,9 @@ __global__ __launch_bounds__(256) void copy_kernel(const float *__restrict__ src
 
 }  // namespace
 
-int64_t linear_tile_elems() { return kTileElems; }
+int64_t linear_tile_elems(bool segmented) {
+  return segmented ? Shape<true>::kTileElems : Shape<false>::kTileElems;
+}
 
 hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h,
                               int64_t n, int64_t ntiles, LinearStatus status, uint32_t epoch,
@@ -667,10 +689,12 @@ hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h
     sg.sh2 = l > 0 ? l - 1 : 0;
   }
   if (seg_len == 0)
-    hipLaunchKernelGGL(linear_scan_kernel<false>, dim3(grid), dim3(kThreads + 64), 0, stream, a,
+    hipLaunchKernelGGL(linear_scan_kernel<false>, dim3(grid), dim3(Shape<false>::kThreads + 64), 0,
+                       stream, a,
                        b, h0, h, n, ntiles, status, epoch, sg);
   else
-    hipLaunchKernelGGL(linear_scan_kernel<true>, dim3(grid), dim3(kThreads + 64), 0, stream, a,
+    hipLaunchKernelGGL(linear_scan_kernel<true>, dim3(grid), dim3(Shape<true>::kThreads + 64), 0,
+                       stream, a,
                        b, h0, h, n, ntiles, status, epoch, sg);
   return hipGetLastError();
 }
@@ -678,10 +702,12 @@ hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h
 int linear_wgs_per_cu() {
   int plain = 0, seg = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &plain, reinterpret_cast<const void *>(linear_scan_kernel<false>), kThreads + 64, 0) !=
+          &plain, reinterpret_cast<const void *>(linear_scan_kernel<false>),
+          Shape<false>::kThreads + 64, 0) !=
           hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &seg, reinterpret_cast<const void *>(linear_scan_kernel<true>), kThreads + 64, 0) !=
+          &seg, reinterpret_cast<const void *>(linear_scan_kernel<true>),
+          Shape<true>::kThreads + 64, 0) !=
           hipSuccess)
     return 0;
   return plain < seg ? plain : seg;

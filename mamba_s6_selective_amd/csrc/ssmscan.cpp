@@ -214,7 +214,7 @@ int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t 
   if (!a || !b || !h) return fail(SSM_ERR_INVALID_ARG, "null pointer with n > 0");
   if (!aligned16(a) || !aligned16(b) || !aligned16(h))
     return fail(SSM_ERR_INVALID_ARG, "a, b and h must be 16-byte aligned");
-  const int64_t tile = linear_tile_elems();
+  const int64_t tile = linear_tile_elems(false);
   const int64_t ntiles = (n + tile - 1) / tile;
   if (ntiles > kLinearMaxTiles)
     return fail(SSM_ERR_UNSUPPORTED, "n too large for one launch (max 2^31 elements)");
@@ -239,7 +239,7 @@ int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, flo
   if (nseq > (int64_t(1) << 31) / len)
     return fail(SSM_ERR_UNSUPPORTED, "nseq * len too large for one launch (max 2^31 elements)");
   const int64_t n = nseq * len;
-  const int64_t tile = linear_tile_elems();
+  const int64_t tile = linear_tile_elems(true);
   const int64_t ntiles = (n + tile - 1) / tile;
   LinearStatus status{};
   uint32_t epoch = 0;

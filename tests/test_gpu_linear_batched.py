@@ -42,11 +42,13 @@ def run(a, b, h0):
     return h.cpu().numpy(), last.cpu().numpy()
 
 
-# sequence lengths below, at and across the lane chunk (4), row (256), tile
-# (8192) and superblock (64 tiles); sequence counts from 1 to thousands
+# sequence lengths below, at and across the lane chunk (4), row (256), wave
+# (768), the batched tile (8448) and superblock (64 tiles), and 8192; sequence
+# counts from 1 to thousands
 SHAPES = [(1, 1), (3, 1), (1000, 1), (5, 2), (7, 3), (9, 4), (4, 5), (33, 255), (17, 256),
-          (6, 257), (3, 8191), (2, 8192), (5, 8193), (4096, 64), (1024, 1000),
-          (2, 64 * 8192 + 3), (1, 100003)]
+          (6, 257), (11, 767), (10, 768), (9, 769), (3, 8191), (2, 8192), (5, 8193),
+          (3, 8447), (2, 8448), (4, 8449), (4096, 64), (1024, 1000), (2, 64 * 8448 + 3),
+          (1, 64 * 8448), (2, 64 * 8192 + 3), (1, 100003)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}" for s in SHAPES])
