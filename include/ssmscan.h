@@ -10,6 +10,18 @@
  *
  * Return codes (ssm_status_t): SSM_OK on success; on any error nothing is
  * launched and ssm_last_error() describes the cause (per calling thread).
+ *
+ * Environment (for experiments and verification):
+ *   SSMSCAN_S6_CHUNK=<steps>       S6 chunk length, read at every call (kept
+ *                                  to at most 256 chunks per sequence; the
+ *                                  rounding then follows the new chunks).
+ *   SSMSCAN_S6_FULL_FIX=1          S6 evaluates every carry term, read at
+ *                                  every call. By default the fix pass skips
+ *                                  terms that are exactly zero in fp32 and
+ *                                  blocks whose correction rounds away; both
+ *                                  settings give bit-identical outputs.
+ *   SSMSCAN_LINEAR_WGS_PER_CU=<k>  caps the workgroups per CU of the single-
+ *                                  pass linear scan (read once per device).
  */
 #ifndef SSMSCAN_H
 #define SSMSCAN_H
