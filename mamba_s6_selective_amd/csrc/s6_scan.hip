@@ -108,6 +108,7 @@ __device__ __forceinline__ void load_row(const T *__restrict__ p, float (&out)[N
 
 struct Geometry {
   int batch, L, d_inner, groups, nchunks, chunk;
+  int nblk;      // blocks of kPrefetch steps in a full chunk
   int full_fix;  // 1: the fix pass evaluates every carry term (no skipped groups or blocks)
 };
 
@@ -125,6 +126,11 @@ __device__ __forceinline__ void decompose(const Geometry &g, int &b, int &c, int
 __device__ __forceinline__ size_t agg_index(const Geometry &g, int NT, int b, int c, int n,
                                             int d) {
   return ((size_t(b) * g.nchunks + c) * NT + n) * g.d_inner + d;
+}
+// Per-block statistics are laid out [b][chunk][block][d], block in the
+// sweep order of their direction.
+__device__ __forceinline__ size_t stat_index(const Geometry &g, int b, int c, int k, int d) {
+  return ((size_t(b) * g.nchunks + c) * g.nblk + k) * g.d_inner + d;
 }
 __device__ __forceinline__ size_t sum_index(const Geometry &g, int b, int c, int d) {
   return (size_t(b) * g.nchunks + c) * g.d_inner + d;
@@ -182,6 +188,25 @@ __device__ __forceinline__ float s6_step(float dt, float x, const Row<T, NT> &Br
   return __builtin_fmaf(Dd, x, acc0 + acc1);
 }
 
+// What one direction's chunk sweep leaves for the fix pass, per full block of
+// kPrefetch steps (sweep order): the running delta sum at the block's end,
+// exactly, and a word holding the block's smallest running sum (high half)
+// and smallest |y| (low half), each truncated to its top 16 bits, i.e. to
+// bf16 toward zero -- never above the true value where that matters (a
+// positive sum, any |y|), so decisions taken from them stay on the safe
+// side. The |y| half is written by the sweep that completes y (0 until
+// then); in a bidirectional call the reverse sweep also writes it into the
+// forward words of the same steps (16-bit stores) when the blocks line up.
+struct SweepStats {
+  float *s_end;
+  uint32_t *word;
+  bool y_final;       // this sweep completes y: record min |y|
+  uint32_t *mirror;   // other direction's words for min |y| (or null)
+};
+__device__ __forceinline__ uint32_t pack_stats(float smin, float ymin) {
+  return (__float_as_uint(smin) & 0xffff0000u) | (__float_as_uint(ymin) >> 16);
+}
+
 // One sweep of the chunk-local recurrence from a zero state. Writes (or, when
 // Accumulate, adds) y for every step of the chunk and leaves the final state
 // in h and the sum of delta in S. Steps run in blocks of kPrefetch with no
@@ -194,7 +219,8 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
                                             const T *__restrict__ B, const T *__restrict__ C,
                                             float *__restrict__ y, const float (&Ap)[NT],
                                             float Dd, const DX &dx, const Geometry &g, int b,
-                                            int d, int t0, int t1, float (&h)[NT], float &S) {
+                                            int c, int d, int t0, int t1, float (&h)[NT],
+                                            float &S, const SweepStats &st) {
 #pragma unroll
   for (int n = 0; n < NT; ++n) h[n] = 0.0f;
   S = 0.0f;
@@ -205,6 +231,16 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
   auto row = [&](int i) { return (row0 + tof(i)) * size_t(g.d_inner); };
   const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));  // input byte offset of the lane
   const uint32_t yo = uint32_t(d) * 4u;                    // output byte offset of the lane
+  // The lane's statistics addresses, formed once: they hold the channel, so
+  // they sit in VGPRs and leave the scalar registers to the B/C rows.
+  const size_t ss = size_t(g.d_inner);
+  const bool stats = st.word != nullptr;
+  float *pe = stats ? st.s_end + stat_index(g, b, c, 0, d) : nullptr;
+  uint32_t *pw = stats ? st.word + stat_index(g, b, c, 0, d) : nullptr;
+  uint16_t *pm = stats && st.mirror && len % kPrefetch == 0
+                     ? reinterpret_cast<uint16_t *>(
+                           st.mirror + stat_index(g, b, c, full / kPrefetch - 1, d))
+                     : nullptr;
   float rd[kPrefetch], rx[kPrefetch], ry[kPrefetch];
   if (full > 0) {
 #pragma unroll
@@ -236,6 +272,7 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
     Row<T, NT> Bc, Cc;
     Bc.load(B + (row0 + tof(i0)) * NT);
     Cc.load(C + (row0 + tof(i0)) * NT);
+    float smin = 0.0f, ymin = 0.0f;
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       Row<T, NT> Bn, Cn;
@@ -244,12 +281,30 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
         Bn.load(B + (row0 + tof(i0 + j + 1)) * NT);
         Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
       }
+      // Keeps the next rows' loads at the head of the step: left to itself the
+      // scheduler may sink them (with their address arithmetic) to just before
+      // the next wait, which then waits for the whole scalar-load latency.
+      __builtin_amdgcn_sched_barrier(0);
       const float out = s6_step<T, NT>(cd[j], cx[j], Bc, Cc, Ap, Dd, h);
-      at(y + row(i0 + j), yo) = Accumulate ? cy[j] + out : out;
+      const float yv = Accumulate ? cy[j] + out : out;
+      at(y + row(i0 + j), yo) = yv;
       S += cd[j];
+      smin = j == 0 ? S : fminf(smin, S);
+      ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
       if (j + 1 < kPrefetch) {
         Bc = Bn;
         Cc = Cn;
+      }
+    }
+    if (stats) {  // wave-uniform
+      // A NaN in the running sum reaches the block's end; fminf would drop it.
+      *pe = S;
+      *pw = pack_stats(S == S ? smin : S, st.y_final ? ymin : 0.0f);
+      pe += ss;
+      pw += ss;
+      if (pm) {  // the mirror runs the other way: its block index falls
+        *pm = uint16_t(__float_as_uint(ymin) >> 16);
+        pm -= 2 * ss;  // 2 halves per 32-bit word
       }
     }
   }
@@ -274,7 +329,8 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
     const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
     float *__restrict__ y, float *__restrict__ agg_s, float *__restrict__ agg_f,
-    float *__restrict__ agg_r, Geometry g, int direction) {
+    float *__restrict__ agg_r, float *__restrict__ sf_end, uint32_t *__restrict__ sf_word,
+    float *__restrict__ sr_end, uint32_t *__restrict__ sr_word, Geometry g, int direction) {
   int b, c, d;
   decompose(g, b, c, d);
   if (d >= g.d_inner) return;
@@ -288,8 +344,13 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
   float h[NT];
   float S = 0.0f;
   const bool multi = g.nchunks > 1;
+  // Statistics for the fix pass, which runs only with several chunks.
+  const SweepStats stf{sf_end, multi ? sf_word : nullptr, direction == SSM_DIR_FWD, nullptr};
+  const SweepStats str{sr_end, multi ? sr_word : nullptr, true,
+                       direction == SSM_DIR_BIDIR ? sf_word : nullptr};
   if (direction != SSM_DIR_REV) {
-    chunk_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, h, S);
+    chunk_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1, h, S,
+                                     stf);
     if (multi) {
       agg_s[sum_index(g, b, c, d)] = S;
 #pragma unroll
@@ -298,9 +359,11 @@ __global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
   }
   if (direction != SSM_DIR_FWD) {
     if (direction == SSM_DIR_BIDIR)
-      chunk_sweep<T, NT, true, true>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, h, S);
+      chunk_sweep<T, NT, true, true>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1, h, S,
+                                     str);
     else
-      chunk_sweep<T, NT, true, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, h, S);
+      chunk_sweep<T, NT, true, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1, h, S,
+                                      str);
     if (multi) {
       if (direction == SSM_DIR_REV) agg_s[sum_index(g, b, c, d)] = S;
 #pragma unroll
@@ -428,18 +491,16 @@ struct FixGroups {
       any_keep = any_keep || keep[g];
     }
   }
-  // Decides what a block of kPrefetch steps with running sums Sj and current
-  // outputs cy needs. Returns 0 when the block leaves y unchanged; otherwise
-  // bit g is set when group g has a lane whose term may be non-zero.
-  // cscale = maxC * kNegligible (infinite when C holds a non-finite value,
-  // or to leave the negligible-block test out).
-  __device__ __forceinline__ uint32_t live(const float (&Sj)[kPrefetch],
-                                           const float (&cy)[kPrefetch], float cscale) const {
-    float smin = Sj[0];
-#pragma unroll
-    for (int j = 1; j < kPrefetch; ++j) smin = fminf(smin, Sj[j]);
-    // A NaN in the sum reaches the block's last step; fminf would drop it.
-    const bool sane = Sj[kPrefetch - 1] == Sj[kPrefetch - 1];
+  // Decides what a block of kPrefetch steps needs, from the chunk pass's
+  // statistics word (smallest running sum and smallest |y| over the block,
+  // both truncated toward zero). Returns 0 when the block leaves y
+  // unchanged; otherwise bit g is set when group g has a lane whose term may
+  // be non-zero. cscale = maxC * kNegligible (infinite when C holds a
+  // non-finite value, or to leave the negligible-block test out).
+  __device__ __forceinline__ uint32_t decide(uint32_t word, float cscale) const {
+    const float smin = __uint_as_float(word & 0xffff0000u);
+    const float ymin = __uint_as_float(word << 16);
+    const bool sane = smin == smin;  // a NaN in the running sum reaches this
     float p[kCount];
 #pragma unroll
     for (int g = 0; g < kCount; ++g) p[g] = Ag[g] * smin;
@@ -449,10 +510,7 @@ struct FixGroups {
       for (int g = 0; g < kCount; ++g) bound = fmaf(cabs[g], exp2_hw(p[g]), bound);
       const float t = bound * cscale;
       const float thr = (sane && !any_keep && t == t) ? fmaxf(t, kTinyY) : __builtin_inff();
-      bool resolved = true;
-#pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) resolved = resolved && fabsf(cy[j]) > thr;
-      if (__builtin_amdgcn_ballot_w64(!resolved) == 0) return 0;
+      if (__builtin_amdgcn_ballot_w64(!(ymin > thr)) == 0) return 0;
     }
     uint32_t m = 0;
 #pragma unroll
@@ -518,60 +576,123 @@ __device__ __forceinline__ float fix_step(float S, const Row<T, NT> &Cr, const f
   return acc0 + acc1;
 }
 
+// Blocks whose statistics words are decided together; the words of the next
+// window are loaded while the current one is worked on.
+constexpr int kFixWindow = 8;
+
+// The fix pass over one chunk in one direction. Blocks are decided from the
+// chunk pass's statistics, a window at a time, without touching delta or y;
+// delta, y and the running sum before the block are loaded only for blocks
+// that change y, the next such block's while the current one computes. The
+// running sums start from the chunk pass's exact values, so every step sees
+// the same sum the sequential sweep would. With ymirror, y changes are also
+// recorded in the other direction's words (min |y| of the new values), which
+// that direction's later fix reads. A tail of fewer than kPrefetch steps is
+// always evaluated in full.
 template <typename T, int NT, bool Reverse, class DX>
 __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *__restrict__ C,
                                           float *__restrict__ y, const float (&Ap)[NT],
                                           const float (&cin)[NT], const DX &dx,
-                                          const Geometry &g, int b, int d, int t0, int t1) {
+                                          const Geometry &g, int b, int c, int d, int t0,
+                                          int t1, const float *__restrict__ s_end,
+                                          const uint32_t *__restrict__ word,
+                                          uint32_t *__restrict__ ymirror) {
   const size_t row0 = size_t(b) * g.L;
   const int len = t1 - t0;
-  const int full = len - len % kPrefetch;
+  const int nfull = len / kPrefetch;
+  const int full = nfull * kPrefetch;
   auto tof = [&](int i) { return Reverse ? (t1 - 1 - i) : (t0 + i); };
   auto row = [&](int i) { return (row0 + tof(i)) * size_t(g.d_inner); };
   const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));
   const uint32_t yo = uint32_t(d) * 4u;
+  const size_t s0 = stat_index(g, b, c, 0, d);
+  const size_t ss = size_t(g.d_inner);  // stride between blocks of the statistics
+  const bool mirror = ymirror && len % kPrefetch == 0;
   const FixGroups<NT> groups(Ap, cin);
   // Short chunks end before their carry has decayed far enough: no test.
   const float cscale = (len >= kNegligibleMinLen && !g.full_fix)
                            ? chunk_cscale<T, NT>(C, (row0 + t0) * NT, len * NT)
                            : __builtin_inff();
-  float rd[kPrefetch], ry[kPrefetch];
-  if (full > 0) {
+  // Loads what block k needs into (dr, yr, s_in): its delta and y words and
+  // the running sum before it.
+  auto load_block = [&](int k, float (&dr)[kPrefetch], float (&yr)[kPrefetch], float &s_in) {
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      rd[j] = ldv(&at(delta + row(j), io));
-      ry[j] = at(y + row(j), yo);
+      dr[j] = ldv(&at(delta + row(k * kPrefetch + j), io));
+      yr[j] = at(y + row(k * kPrefetch + j), yo);
     }
-  }
-  float S = 0.0f;
-  for (int i0 = 0; i0 < full; i0 += kPrefetch) {
-    float Sj[kPrefetch], cy[kPrefetch];
+    s_in = k > 0 ? s_end[s0 + size_t(k - 1) * ss] : 0.0f;
+  };
+  // Evaluates block k from its loaded words for the groups in live.
+  auto run_block = [&](int k, const float (&dr)[kPrefetch], const float (&yr)[kPrefetch],
+                       float S, uint32_t live) {
+    float Sj[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      S += dx(rd[j]);  // transformed when used: its load has had a block of steps to land
+      S += dx(dr[j]);
       Sj[j] = S;
-      cy[j] = ry[j];
     }
-    if (i0 + kPrefetch < full) {
-#pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) {
-        rd[j] = ldv(&at(delta + row(i0 + kPrefetch + j), io));
-        ry[j] = at(y + row(i0 + kPrefetch + j), yo);
-      }
-    }
-    const uint32_t live = g.full_fix ? ~0u : groups.live(Sj, cy, cscale);
-    if (live == 0) continue;  // the block leaves y as it is
+    const int i0 = k * kPrefetch;
     Row<T, NT> Cc;
     Cc.load(C + (row0 + tof(i0)) * NT);
+    float ymin = 0.0f;
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       Row<T, NT> Cn;
       wait_scalar_loads();
       if (j + 1 < kPrefetch) Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
-      at(y + row(i0 + j), yo) = cy[j] + fix_step<T, NT, true>(Sj[j], Cc, Ap, cin, live);
+      const float yv = yr[j] + fix_step<T, NT, true>(Sj[j], Cc, Ap, cin, live);
+      at(y + row(i0 + j), yo) = yv;
+      ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
       if (j + 1 < kPrefetch) Cc = Cn;
     }
+    if (mirror)
+      reinterpret_cast<uint16_t *>(ymirror + s0 + size_t(nfull - 1 - k) * ss)[0] =
+          uint16_t(__float_as_uint(ymin) >> 16);
+  };
+
+  uint32_t wn[kFixWindow];  // statistics words of the next window
+#pragma unroll
+  for (int i = 0; i < kFixWindow; ++i) wn[i] = i < nfull ? word[s0 + size_t(i) * ss] : 0u;
+  for (int w0 = 0; w0 < nfull; w0 += kFixWindow) {
+    // Decide the window: 4 bits of live groups per block.
+    uint32_t masks = 0;
+#pragma unroll
+    for (int i = 0; i < kFixWindow; ++i) {
+      if (w0 + i < nfull) {
+        const uint32_t m = g.full_fix ? 0xfu : groups.decide(wn[i], cscale);
+        masks |= m << (4 * i);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kFixWindow; ++i) {
+      const int k = w0 + kFixWindow + i;
+      if (k < nfull) wn[i] = word[s0 + size_t(k) * ss];
+    }
+    if (masks == 0) continue;  // wave-uniform: the whole window leaves y as it is
+    // Its blocks that change y, each one's words loaded while the one before
+    // it computes.
+    int i = __builtin_ctz(masks) / 4;
+    float dr[kPrefetch], yr[kPrefetch], s_in;
+    load_block(w0 + i, dr, yr, s_in);
+    for (;;) {
+      const uint32_t live = (masks >> (4 * i)) & 0xfu;
+      masks &= ~(0xfu << (4 * i));
+      const int inext = masks ? __builtin_ctz(masks) / 4 : -1;
+      float dn[kPrefetch], yn[kPrefetch], sn = 0.0f;
+      if (inext >= 0) load_block(w0 + inext, dn, yn, sn);
+      run_block(w0 + i, dr, yr, s_in, live);
+      if (inext < 0) break;
+      i = inext;
+#pragma unroll
+      for (int j = 0; j < kPrefetch; ++j) {
+        dr[j] = dn[j];
+        yr[j] = yn[j];
+      }
+      s_in = sn;
+    }
   }
+  float S = nfull > 0 ? s_end[s0 + size_t(nfull - 1) * ss] : 0.0f;
   for (int i = full; i < len; ++i) {
     const size_t r = row(i);
     S += dx(ldv(&at(delta + r, io)));
@@ -587,7 +708,9 @@ __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
     const T *__restrict__ delta, const float *__restrict__ dbias, const float *__restrict__ A,
     const T *__restrict__ C,
     float *__restrict__ y, const float *__restrict__ carry_f,
-    const float *__restrict__ carry_r, Geometry g, int direction) {
+    const float *__restrict__ carry_r, const float *__restrict__ sf_end,
+    const uint32_t *__restrict__ sf_word, const float *__restrict__ sr_end,
+    uint32_t *__restrict__ sr_word, Geometry g, int direction) {
   int b, c, d;
   decompose(g, b, c, d);
   if (d >= g.d_inner) return;
@@ -603,12 +726,15 @@ __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
   if (do_f) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) cin[n] = carry_f[agg_index(g, NT, b, c, n, d)];
-    fix_sweep<T, NT, false>(delta, C, y, Ap, cin, dx, g, b, d, t0, t1);
+    // In a bidirectional call the reverse fix reads min |y| from its own words.
+    fix_sweep<T, NT, false>(delta, C, y, Ap, cin, dx, g, b, c, d, t0, t1, sf_end, sf_word,
+                            direction == SSM_DIR_BIDIR ? sr_word : nullptr);
   }
   if (do_r) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) cin[n] = carry_r[agg_index(g, NT, b, c, n, d)];
-    fix_sweep<T, NT, true>(delta, C, y, Ap, cin, dx, g, b, d, t0, t1);
+    fix_sweep<T, NT, true>(delta, C, y, Ap, cin, dx, g, b, c, d, t0, t1, sr_end, sr_word,
+                           nullptr);
   }
 }
 
@@ -662,19 +788,22 @@ int launch_all(const S6Args &a, hipStream_t stream) {
   const char *full = getenv("SSMSCAN_S6_FULL_FIX");
   g.full_fix = (full && atoi(full) != 0) ? 1 : 0;
   g.nchunks = (a.L + g.chunk - 1) / g.chunk;
+  g.nblk = g.chunk / kPrefetch;
   const int64_t wgs = int64_t(g.groups) * g.nchunks * a.batch;
   if (wgs > (int64_t(1) << 31) - 1) return fail(SSM_ERR_UNSUPPORTED, "problem too large");
 
   float *agg_s = nullptr, *agg_f = nullptr, *agg_r = nullptr, *car_f = nullptr,
-        *car_r = nullptr;
+        *car_r = nullptr, *sf_end = nullptr, *sr_end = nullptr;
+  uint32_t *sf_word = nullptr, *sr_word = nullptr;
   if (g.nchunks > 1) {
     const size_t per = size_t(a.batch) * g.nchunks * NT * a.d_inner;
     const size_t sums = (size_t(a.batch) * g.nchunks * a.d_inner + 63) / 64 * 64;
+    const size_t stats = (size_t(a.batch) * g.nchunks * g.nblk * a.d_inner + 63) / 64 * 64;
     void *buf = nullptr;
     unsigned long long *ticket = nullptr, base = 0;
     uint32_t epoch = 0;
-    if (int rc = s6_workspace(stream, (4 * per + sums) * sizeof(float), 0, &buf, &ticket, &base,
-                              &epoch))
+    if (int rc = s6_workspace(stream, (4 * per + sums + 4 * stats) * sizeof(float), 0, &buf,
+                              &ticket, &base, &epoch))
       return rc;
     float *f = static_cast<float *>(buf);
     agg_s = f;
@@ -682,14 +811,18 @@ int launch_all(const S6Args &a, hipStream_t stream) {
     agg_r = agg_f + per;
     car_f = agg_r + per;
     car_r = car_f + per;
+    sf_end = car_r + per;
+    sf_word = reinterpret_cast<uint32_t *>(sf_end + stats);
+    sr_end = sf_end + 2 * stats;
+    sr_word = reinterpret_cast<uint32_t *>(sf_end + 3 * stats);
   }
   const T *u = static_cast<const T *>(a.u);
   const T *dl = static_cast<const T *>(a.delta);
   const T *B = static_cast<const T *>(a.B);
   const T *C = static_cast<const T *>(a.C);
   hipLaunchKernelGGL((s6_chunk_kernel<T, NT, DX>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
-                     u, dl, a.delta_bias, a.A, B, C, a.D, a.y, agg_s, agg_f, agg_r, g,
-                     a.direction);
+                     u, dl, a.delta_bias, a.A, B, C, a.D, a.y, agg_s, agg_f, agg_r, sf_end,
+                     sf_word, sr_end, sr_word, g, a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 chunk launch")) return rc;
   if (g.nchunks == 1) return SSM_OK;
   const int parts = (g.nchunks + kCarryPart - 1) / kCarryPart;
@@ -698,7 +831,8 @@ int launch_all(const S6Args &a, hipStream_t stream) {
                      agg_s, agg_f, agg_r, a.A, car_f, car_r, g, NT, a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 carry launch")) return rc;
   hipLaunchKernelGGL((s6_fix_kernel<T, NT, DX>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
-                     dl, a.delta_bias, a.A, C, a.y, car_f, car_r, g, a.direction);
+                     dl, a.delta_bias, a.A, C, a.y, car_f, car_r, sf_end, sf_word, sr_end,
+                     sr_word, g, a.direction);
   return hip_check(hipGetLastError(), "s6 fix launch");
 }
 
