@@ -181,6 +181,10 @@ FULL_FIX = [  # (batch, L, d_inner, dtype, chunk, fused)
     (2, 4096, 320, "f32", "1024", False),
     (1, 6000, 256, "bf16", "512", True),
     (4, 2048, 1536, "bf16", "160", False),
+    # last chunks of 187 and 45 steps: a tail after the full blocks, and in
+    # the bidirectional call blocks that do not line up between directions
+    (2, 3003, 192, "f32", "256", False),
+    (1, 2093, 320, "bf16", "128", True),
 ]
 
 
