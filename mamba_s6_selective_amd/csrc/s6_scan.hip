@@ -17,15 +17,19 @@
 // The sequence is split into chunks so that enough lanes run (L-splitting):
 //  1. chunk pass: every chunk runs its recurrence from a zero state, writes
 //     its local y (with the D*u term), the sum of delta over the chunk per d
-//     (the chunk's multiplier for state n is exp(A[d,n] * that sum)) and the
-//     local end state per (d, n) (reverse: the local state at the chunk start).
+//     (the chunk's multiplier for state n is exp(A[d,n] * that sum)), the
+//     local end state per (d, n) (reverse: the local state at the chunk
+//     start) and small per-block statistics for the fix pass.
 //  2. carry pass: per (b, n, d), a left fold over the chunk aggregates gives
 //     each chunk's incoming state (forward and/or reverse); the fold is split
-//     over waves (parts of up to 32 chunks) joined through LDS.
+//     over waves (parts of kCarryPart chunks) joined through LDS.
 //  3. fix pass: every chunk except the first (forward) / last (reverse) adds
 //     sum_n C[t,n] * carry_n * exp(A_n * S_t), S_t the running sum of delta
 //     from the carry's entry point, to its y. This is the exact carry
-//     contribution (the state is linear in its initial value).
+//     contribution (the state is linear in its initial value); terms that
+//     are exactly zero in fp32, and blocks whose whole contribution rounds
+//     away against y, are skipped, with results bit-identical to evaluating
+//     them.
 // All three passes are deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -208,8 +212,9 @@ __device__ __forceinline__ uint32_t pack_stats(float smin, float ymin) {
 }
 
 // One sweep of the chunk-local recurrence from a zero state. Writes (or, when
-// Accumulate, adds) y for every step of the chunk and leaves the final state
-// in h and the sum of delta in S. Steps run in blocks of kPrefetch with no
+// Accumulate, adds) y for every step of the chunk, the block statistics in
+// st (when st.word is set), and leaves the final state in h and the sum of
+// delta in S. Steps run in blocks of kPrefetch with no
 // branch inside a block (so the compiler can overlap neighbouring steps), and
 // each lane's words for the next block are loaded while the current block
 // computes; B[t] and C[t] are wave-uniform scalar loads. A tail of fewer than
