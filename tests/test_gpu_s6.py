@@ -176,29 +176,32 @@ def _s6_any(inp, direction, fused):
     return y.cpu().numpy()
 
 
-FULL_FIX = [  # (batch, L, d_inner, dtype, chunk, fused)
-    (1, 8192, 512, "bf16", "256", False),
-    (2, 4096, 320, "f32", "1024", False),
-    (1, 6000, 256, "bf16", "512", True),
-    (4, 2048, 1536, "bf16", "160", False),
+FULL_FIX = [  # (batch, L, d_inner, N, dtype, chunk, fused)
+    (1, 8192, 512, 16, "bf16", "256", False),
+    (2, 4096, 320, 16, "f32", "1024", False),
+    (1, 6000, 256, 16, "bf16", "512", True),
+    (4, 2048, 1536, 16, "bf16", "160", False),
     # last chunks of 187 and 45 steps: a tail after the full blocks, and in
     # the bidirectional call blocks that do not line up between directions
-    (2, 3003, 192, "f32", "256", False),
-    (1, 2093, 320, "bf16", "128", True),
+    (2, 3003, 192, 16, "f32", "256", False),
+    (1, 2093, 320, 16, "bf16", "128", True),
+    # partly filled waves (36 and 1 active lanes) and a short last state group
+    (1, 4096, 100, 7, "bf16", "256", False),
+    (2, 3000, 257, 16, "f32", "512", True),
 ]
 
 
-@pytest.mark.parametrize("case", FULL_FIX, ids=[f"b{c[0]}_L{c[1]}_d{c[2]}_{c[3]}_c{c[4]}"
-                                                 f"{'_fused' if c[5] else ''}" for c in FULL_FIX])
+@pytest.mark.parametrize("case", FULL_FIX, ids=[f"b{c[0]}_L{c[1]}_d{c[2]}_N{c[3]}_{c[4]}_c{c[5]}"
+                                                 f"{'_fused' if c[6] else ''}" for c in FULL_FIX])
 def test_s6_fix_shortcuts_are_exact(case, monkeypatch):
     """The fix pass's skipped carry groups and left-alone blocks change no
     output bit: the result equals, value for value, the one with every carry
     term evaluated. Some channels get tiny outputs (D = 0 and small u), whose
     blocks the negligible-block test must not leave alone."""
-    b, L, d, dt, chunk, fused = case
+    b, L, d, N, dt, chunk, fused = case
     say(f"s6 fix shortcuts exact {case}")
     monkeypatch.setenv("SSMSCAN_S6_CHUNK", chunk)
-    inp = s6_inputs(b, L, d, 16, seed=L + d, dtype=dt)
+    inp = s6_inputs(b, L, d, N, seed=L + d, dtype=dt)
     inp.D = inp.D.clone()
     inp.D[::7] = 0.0
     inp.u[:, :, ::7] = (inp.u[:, :, ::7].float() * 1e-6).to(inp.u.dtype)
