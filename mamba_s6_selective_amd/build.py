@@ -1,12 +1,17 @@
 """Builds libssmscan.so (HIP, gfx950) in place, next to this file.
 
     python -m mamba_s6_selective_amd.build
+
+Each source compiles to an object in parallel; the objects are then linked
+into the shared library, which replaces the old one only once complete.
 """
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -17,10 +22,11 @@ SOURCES = ["ssmscan.cpp", "linear_scan.hip", "linear_3pass.hip", "s6_scan.hip"]
 # Packed-FP32 instructions are switched off for every HIP source; the
 # compiler otherwise forms them on its own from scalar float code.
 HIPCC_FLAGS = [
-    "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+    "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
+LINK_FLAGS = ["--offload-arch=gfx950", "-fPIC", "-shared"]
 
 
 def hipcc() -> str:
@@ -30,16 +36,35 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> Path:
-    tmp = LIB.with_suffix(".so.tmp%d" % os.getpid())
-    cmd = [hipcc(), *HIPCC_FLAGS, *[str(CSRC / s) for s in SOURCES], "-o", str(tmp)]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libssmscan.so")
-    if verbose:
-        sys.stderr.write(res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    work = Path(tempfile.mkdtemp(prefix="ssmscan_build_"))
+    try:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = work / (Path(src).stem + ".o")
+            objs.append(obj)
+            cmd = [hipcc(), *HIPCC_FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                stderr=subprocess.PIPE, text=True)))
+        failed = False
+        for src, p in procs:
+            out, err = p.communicate()
+            if p.returncode != 0:
+                sys.stderr.write(f"--- {src}\n{out}{err}")
+                failed = True
+            elif verbose:
+                sys.stderr.write(err)
+        if failed:
+            raise RuntimeError("hipcc failed building libssmscan.so")
+        tmp = LIB.with_suffix(".so.tmp%d" % os.getpid())
+        res = subprocess.run([hipcc(), *LINK_FLAGS, *map(str, objs), "-o", str(tmp)],
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError("hipcc failed linking libssmscan.so")
+        os.replace(tmp, LIB)
+        return LIB
+    finally:
+        shutil.rmtree(work, ignore_errors=True)
 
 
 if __name__ == "__main__":
