@@ -249,6 +249,40 @@ def cpu_baseline(budget_s):
                       f"(median {med:.3f} s)"}
 
 
+def cpu_baseline_s6(name, budget_s):
+    """The float64 C oracle on a bounded sample of an S6 workload: the first
+    k (batch, channel) sequences over all L steps, k doubled until one pass
+    takes about budget_s / 4, then repeated for about budget_s seconds."""
+    import numpy as np
+    from mamba_s6_selective_amd.workloads import S6_WORKLOADS, s6_workload_inputs
+    from oracle import native
+    w = S6_WORKLOADS[name]
+    u, dl, A, B, C, D = s6_workload_inputs(name).as_f64()
+    channels = w["batch"] * w["d_inner"]
+    out = np.empty(u.shape, dtype=np.float64)
+    native.load()
+
+    def one(k):
+        t0 = time.perf_counter()
+        _, used = native.selective_scan(u, dl, A, B, C, D, w["direction"], 0, k, 0, out)
+        return time.perf_counter() - t0, used
+
+    k = 8
+    dt, used = one(k)
+    while dt < budget_s / 4 and k < channels:
+        k = min(channels, 2 * k)
+        dt, used = one(k)
+    times = [dt]
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end and len(times) < 20:
+        times.append(one(k)[0])
+    med = statistics.median(times)
+    return {"value": k * w["L"] / med, "unit": "elements/s", "cores": used, "kind": "oracle",
+            "sample": f"(batch, channel) sequences [0, {k}) of {channels}, all {w['L']} steps "
+                      f"({w['direction']}), float64 C loop over OpenMP threads, {len(times)} passes "
+                      f"(median {med:.3f} s)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +351,10 @@ def main():
                 f"alu frac {r['roofline']['frac']:.3f}, hbm frac {r['hbm']['frac_of_8TBs']:.3f}")
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        for r in record.get("s6", []):
+            r["cpu_baseline"] = cpu_baseline_s6(r["workload"], args.cpu_seconds / 4)
+            log(f"{r['workload']}: oracle {r['cpu_baseline']['value']:.3g} elements/s on "
+                f"{r['cpu_baseline']['cores']} threads")
     print(json.dumps(record), flush=True)
 
 
