@@ -249,6 +249,28 @@ def cpu_baseline(budget_s):
                       f"(median {med:.3f} s)"}
 
 
+def cpu_baseline_batched(budget_s, nseq=4096, length=32768):
+    """The float64 C oracle on the batched form of the same 2^27 elements:
+    one sequential loop per sequence (h0 = 0), over as many sequences as
+    about budget_s allows."""
+    import numpy as np
+    from mamba_s6_selective_amd.workloads import linear_workload_inputs
+    from oracle import native
+    a, b = linear_workload_inputs(LINEAR_WORKLOAD)
+    a = a.numpy().astype(np.float64).reshape(nseq, length)
+    b = b.numpy().astype(np.float64).reshape(nseq, length)
+    native.load()
+    done = 0
+    t0 = time.perf_counter()
+    while done < nseq and (done == 0 or time.perf_counter() - t0 < budget_s):
+        native.linear_scan(a[done], b[done], 0.0)
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done * length / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequences [0, {done}) of {nseq} x {length}, float64 C loop, "
+                      f"{dt:.2f} s"}
+
+
 def cpu_baseline_s6(name, budget_s):
     """The float64 C oracle on a bounded sample of an S6 workload: the first
     k (batch, channel) sequences over all L steps, k doubled until one pass
@@ -351,6 +373,9 @@ def main():
                 f"alu frac {r['roofline']['frac']:.3f}, hbm frac {r['hbm']['frac_of_8TBs']:.3f}")
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        # the three-pass scan computes the same workload: the same oracle run
+        record["three_pass"]["cpu_baseline"] = record["cpu_baseline"]
+        record["batched"]["cpu_baseline"] = cpu_baseline_batched(args.cpu_seconds / 4)
         for r in record.get("s6", []):
             r["cpu_baseline"] = cpu_baseline_s6(r["workload"], args.cpu_seconds / 4)
             log(f"{r['workload']}: oracle {r['cpu_baseline']['value']:.3g} elements/s on "
