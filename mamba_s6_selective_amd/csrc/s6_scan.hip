@@ -533,20 +533,21 @@ struct FixGroups {
 // bit patterns, reduced with a wave-wide unsigned max. A NaN or infinity
 // gives +inf.
 template <typename T, int NT>
-__device__ __forceinline__ float chunk_cscale(const T *__restrict__ C, size_t first, int count) {
-  const uint32_t lane = __lane_id();
-  const uint32_t nact = uint32_t(__popcll(__builtin_amdgcn_read_exec()));
+__device__ __forceinline__ float chunk_cscale(const T *__restrict__ C, size_t first,
+                                              size_t count) {
+  const size_t lane = __lane_id();
+  const size_t nact = size_t(__popcll(__builtin_amdgcn_read_exec()));
   uint32_t m = 0;
   if constexpr (sizeof(T) == 2 && NT % 2 == 0) {
     // bf16 rows of even length: 32-bit words of two values each (first is even).
     const uint32_t *w = reinterpret_cast<const uint32_t *>(C + first);
-    const uint32_t words = uint32_t(count) / 2;
-    for (uint32_t i = lane; i < words; i += nact) {
+    const size_t words = count / 2;
+    for (size_t i = lane; i < words; i += nact) {
       const uint32_t x = w[i];
       m = max(m, max((x << 16) & 0x7fffffffu, x & 0x7fff0000u));
     }
   } else {
-    for (uint32_t i = lane; i < uint32_t(count); i += nact) {
+    for (size_t i = lane; i < count; i += nact) {
       uint32_t x;
       if constexpr (sizeof(T) == 2)
         x = uint32_t(C[first + i]) << 16;
@@ -616,7 +617,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   const FixGroups<NT> groups(Ap, cin);
   // Short chunks end before their carry has decayed far enough: no test.
   const float cscale = (len >= kNegligibleMinLen && !g.full_fix)
-                           ? chunk_cscale<T, NT>(C, (row0 + t0) * NT, len * NT)
+                           ? chunk_cscale<T, NT>(C, (row0 + t0) * NT, size_t(len) * NT)
                            : __builtin_inff();
   // Loads what block k needs into (dr, yr, s_in): its delta and y words and
   // the running sum before it.
