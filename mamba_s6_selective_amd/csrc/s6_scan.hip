@@ -527,34 +527,55 @@ struct FixGroups {
   }
 };
 
-// maxC * kNegligible for the chunk's C rows [first, first + count) (element
-// offsets), the same in every lane: the rows are read as words spread over
-// the wave's active lanes (a prefix of the wave) and their magnitudes, as
-// bit patterns, reduced with a wave-wide unsigned max. A NaN or infinity
-// gives +inf.
-template <typename T, int NT>
-__device__ __forceinline__ float chunk_cscale(const T *__restrict__ C, size_t first,
-                                              size_t count) {
+// Largest mag(p[i]) over i in [0, count), each lane of the wave's active
+// lanes (a prefix of the wave) taking every nact-th item; four loads per lane
+// are in flight at a time (one at a time would cost a memory round trip per
+// item a lane reads).
+template <class V, class Mag>
+__device__ __forceinline__ uint32_t lanes_max(const V *__restrict__ p, size_t count, Mag mag) {
   const size_t lane = __lane_id();
   const size_t nact = size_t(__popcll(__builtin_amdgcn_read_exec()));
   uint32_t m = 0;
-  if constexpr (sizeof(T) == 2 && NT % 2 == 0) {
-    // bf16 rows of even length: 32-bit words of two values each (first is even).
-    const uint32_t *w = reinterpret_cast<const uint32_t *>(C + first);
-    const size_t words = count / 2;
-    for (size_t i = lane; i < words; i += nact) {
-      const uint32_t x = w[i];
-      m = max(m, max((x << 16) & 0x7fffffffu, x & 0x7fff0000u));
+  for (size_t i0 = lane; i0 < count; i0 += 4 * nact) {
+    V r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const size_t i = i0 + k * nact;
+      r[k] = i < count ? p[i] : V{};
     }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, mag(r[k]));
+  }
+  return m;
+}
+
+// maxC * kNegligible for the chunk's C rows [first, first + count) (element
+// offsets, whole rows), the same in every lane: the magnitudes, as bit
+// patterns, reduced over the wave's active lanes and then wave-wide with an
+// unsigned max. Rows of whole 16-byte vectors (C is 16-byte aligned) are read
+// as vectors, bf16 rows of even length as pairs. A NaN or infinity gives +inf.
+template <typename T, int NT>
+__device__ __forceinline__ float chunk_cscale(const T *__restrict__ C, size_t first,
+                                              size_t count) {
+  auto mag32 = [](uint32_t x) -> uint32_t {  // a 32-bit word: one fp32 or two bf16
+    if constexpr (sizeof(T) == 2)
+      return max((x << 16) & 0x7fffffffu, x & 0x7fff0000u);
+    else
+      return x & 0x7fffffffu;
+  };
+  uint32_t m;
+  if constexpr (NT * sizeof(T) % 16 == 0) {
+    m = lanes_max(reinterpret_cast<const uint4 *>(C + first), count * sizeof(T) / 16,
+                  [&](const uint4 &v) {
+                    return max(max(mag32(v.x), mag32(v.y)), max(mag32(v.z), mag32(v.w)));
+                  });
+  } else if constexpr (sizeof(T) == 2 && NT % 2 == 0) {
+    m = lanes_max(reinterpret_cast<const uint32_t *>(C + first), count / 2, mag32);
+  } else if constexpr (sizeof(T) == 2) {
+    m = lanes_max(C + first, count,
+                  [](uint16_t x) { return (uint32_t(x) << 16) & 0x7fffffffu; });
   } else {
-    for (size_t i = lane; i < count; i += nact) {
-      uint32_t x;
-      if constexpr (sizeof(T) == 2)
-        x = uint32_t(C[first + i]) << 16;
-      else
-        x = __float_as_uint(C[first + i]);
-      m = max(m, x & 0x7fffffffu);
-    }
+    m = lanes_max(reinterpret_cast<const uint32_t *>(C + first), count, mag32);
   }
   m = __ockl_wfred_max_u32(m);
   return m >= 0x7f800000u ? __builtin_inff() : __uint_as_float(m) * kNegligible;
@@ -594,13 +615,14 @@ constexpr int kFixWindow = 8;
 // the same sum the sequential sweep would. With ymirror, y changes are also
 // recorded in the other direction's words (min |y| of the new values), which
 // that direction's later fix reads. A tail of fewer than kPrefetch steps is
-// always evaluated in full.
+// always evaluated in full. cscale is chunk_cscale of the chunk's C rows, or
+// +inf to leave the negligible-block test out.
 template <typename T, int NT, bool Reverse, class DX>
 __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *__restrict__ C,
                                           float *__restrict__ y, const float (&Ap)[NT],
                                           const float (&cin)[NT], const DX &dx,
                                           const Geometry &g, int b, int c, int d, int t0,
-                                          int t1, const float *__restrict__ s_end,
+                                          int t1, float cscale, const float *__restrict__ s_end,
                                           const uint32_t *__restrict__ word,
                                           uint32_t *__restrict__ ymirror) {
   const size_t row0 = size_t(b) * g.L;
@@ -615,10 +637,6 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   const size_t ss = size_t(g.d_inner);  // stride between blocks of the statistics
   const bool mirror = ymirror && len % kPrefetch == 0;
   const FixGroups<NT> groups(Ap, cin);
-  // Short chunks end before their carry has decayed far enough: no test.
-  const float cscale = (len >= kNegligibleMinLen && !g.full_fix)
-                           ? chunk_cscale<T, NT>(C, (row0 + t0) * NT, size_t(len) * NT)
-                           : __builtin_inff();
   // Loads what block k needs into (dr, yr, s_in): its delta and y words and
   // the running sum before it.
   auto load_block = [&](int k, float (&dr)[kPrefetch], float (&yr)[kPrefetch], float &s_in) {
@@ -729,18 +747,24 @@ __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
 #pragma unroll
   for (int n = 0; n < NT; ++n) Ap[n] = A[size_t(d) * NT + n] * kLog2e;
   const DX dx = make_dx<DX>(dbias, d);
+  // Short chunks end before their carry has decayed far enough: no
+  // negligible-block test.
+  const float cscale =
+      (t1 - t0 >= kNegligibleMinLen && !g.full_fix)
+          ? chunk_cscale<T, NT>(C, (size_t(b) * g.L + t0) * NT, size_t(t1 - t0) * NT)
+          : __builtin_inff();
   if (do_f) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) cin[n] = carry_f[agg_index(g, NT, b, c, n, d)];
     // In a bidirectional call the reverse fix reads min |y| from its own words.
-    fix_sweep<T, NT, false>(delta, C, y, Ap, cin, dx, g, b, c, d, t0, t1, sf_end, sf_word,
-                            direction == SSM_DIR_BIDIR ? sr_word : nullptr);
+    fix_sweep<T, NT, false>(delta, C, y, Ap, cin, dx, g, b, c, d, t0, t1, cscale, sf_end,
+                            sf_word, direction == SSM_DIR_BIDIR ? sr_word : nullptr);
   }
   if (do_r) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) cin[n] = carry_r[agg_index(g, NT, b, c, n, d)];
-    fix_sweep<T, NT, true>(delta, C, y, Ap, cin, dx, g, b, c, d, t0, t1, sr_end, sr_word,
-                           nullptr);
+    fix_sweep<T, NT, true>(delta, C, y, Ap, cin, dx, g, b, c, d, t0, t1, cscale, sr_end,
+                           sr_word, nullptr);
   }
 }
 

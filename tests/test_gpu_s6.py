@@ -188,6 +188,11 @@ FULL_FIX = [  # (batch, L, d_inner, N, dtype, chunk, fused)
     # partly filled waves (36 and 1 active lanes) and a short last state group
     (1, 4096, 100, 7, "bf16", "256", False),
     (2, 3000, 257, 16, "f32", "512", True),
+    # C rows that are not whole 16-byte vectors (bf16 pairs, single fp32
+    # values) and fp32 rows of two vectors, for the chunk's max |C|
+    (1, 3000, 64, 6, "bf16", "200", False),
+    (1, 2500, 96, 5, "f32", "128", False),
+    (2, 2048, 128, 8, "f32", "128", False),
 ]
 
 
