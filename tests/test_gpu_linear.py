@@ -110,6 +110,24 @@ def test_linear_full_size_workload():
     assert_close(h.cpu().numpy(), ref, TOL, "linear-n134217728")
 
 
+def test_linear_homogeneous_bit_exact_full_size():
+    """h is linear in (b, h0), and doubling both doubles every product and
+    sum without a new rounding (no value here is near under- or overflow):
+    h(a, 2b, 2h0) equals 2 h(a, b, h0) bit for bit at 2^27 elements, however
+    the look-back groups the fold."""
+    say("linear-n134217728: h(a, 2b, 2h0) == 2 h(a, b, h0)")
+    dev = need_gpu()
+    a, b = linear_workload_inputs("linear-n134217728")
+    a, b = a.to(dev), b.to(dev)
+    h1 = ssm.linear_scan(a, b, 0.75)
+    h2 = ssm.linear_scan(a, b * 2, 1.5)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(h1).all())
+    bad = int((h2 != 2 * h1).sum())
+    say(f"  elements not exactly doubled: {bad}")
+    assert bad == 0
+
+
 @pytest.mark.parametrize("n", [1 << 27, (1 << 20) + 3])
 def test_linear_bitwise_determinism_100_runs(n):
     say(f"linear determinism 100 runs n={n}")
