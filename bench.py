@@ -54,13 +54,28 @@ def load_traffic(kind, *kernel_srcs):
     return d.get("bytes_per_launch")
 
 
+# Untimed work before each timed section lasts at least SETTLE["s"] seconds
+# (--settle-seconds). After an idle spell the GPU's clocks ramp for about a second under load: the
+# long S6 workload measured 336-380 us per call over its first 40 calls and
+# 315 us once settled, the 2^27 linear scan 358 us on its first call and
+# 272-285 us before settling at ~273 us.
+SETTLE = {"s": 1.0}
+
+
 def time_steps(fn, steps, warmup):
-    """Runs fn() warmup times, then `steps` timed times with one HIP event pair
-    per step on torch's current stream (where the library launches)."""
+    """Runs fn() warmup times (and on, untimed, until SETTLE["s"] seconds have
+    passed, so that the clocks have settled), then `steps` timed times with
+    one HIP event pair per step on torch's current stream (where the library
+    launches)."""
     import torch
+    t_settle = time.perf_counter() + SETTLE["s"]
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while time.perf_counter() < t_settle:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t0 = time.perf_counter()
@@ -317,7 +332,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--exp-cost", type=float, default=2.0,
                     help="lane-cycles one v_exp_f32 occupies relative to an FMA")
+    ap.add_argument("--settle-seconds", type=float, default=SETTLE["s"],
+                    help="least untimed run time before each timed section (clock ramp)")
     args = ap.parse_args()
+    SETTLE["s"] = args.settle_seconds
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the scan runs on a single device and this "
               "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -349,6 +367,7 @@ def main():
         "value": n / (ms_step * 1e-3),
         "unit": "elements/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle_s": args.settle_seconds,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded; pages' distributions)",
