@@ -128,6 +128,36 @@ def test_linear_homogeneous_bit_exact_full_size():
     assert bad == 0
 
 
+def test_linear_maximum_size_carry_exact():
+    """n = 2^31, the largest length the single-pass scan accepts (every
+    look-back level full: 64 blocks of 64 superblocks of 64 tiles), with
+    a = 1 and b = 1 at 1000 seeded positions, 0 elsewhere: every carry crosses
+    the whole sequence, and h[i] = h0 + (number of ones at positions <= i)
+    exactly in fp32 whatever the grouping. Checked at every tile's last
+    element, at the ones and just before them, and at 2^20 seeded positions."""
+    n = 1 << 31
+    say(f"linear maximum size n={n}: a = 1, sparse integer b")
+    dev = need_gpu()
+    g = torch.Generator().manual_seed(2031)
+    pos = np.unique(torch.randint(0, n, (1000,), generator=g).numpy().astype(np.int64))
+    a = torch.ones(n, device=dev)
+    b = torch.zeros(n, device=dev)
+    b[torch.from_numpy(pos).to(dev)] = 1.0
+    h = ssm.linear_scan(a, b, 0.5)
+    del a, b
+    tile = 8192
+    idx = np.concatenate([
+        np.arange(tile - 1, n, tile, dtype=np.int64), [0, n - 1], pos, np.maximum(pos - 1, 0),
+        torch.randint(0, n, (1 << 20,), generator=g).numpy().astype(np.int64)])
+    got = h[torch.from_numpy(idx).to(dev)].cpu().numpy()
+    del h
+    torch.cuda.synchronize()
+    expected = 0.5 + np.searchsorted(pos, idx, side="right").astype(np.float64)
+    bad = int(np.count_nonzero(got != expected))
+    say(f"  {idx.size} positions checked, {bad} differ")
+    assert bad == 0
+
+
 @pytest.mark.parametrize("n", [1 << 27, (1 << 20) + 3])
 def test_linear_bitwise_determinism_100_runs(n):
     say(f"linear determinism 100 runs n={n}")

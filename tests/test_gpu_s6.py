@@ -11,7 +11,7 @@ import torch
 
 import mamba_s6_selective_amd as ssm
 import oracle
-from gpu_util import assert_close, need_gpu, say
+from gpu_util import assert_close, max_scaled_err, need_gpu, say
 from mamba_s6_selective_amd.workloads import S6_WORKLOADS, s6_inputs, s6_workload_inputs
 from oracle import native
 
@@ -108,6 +108,41 @@ def test_s6_single_state_equals_linear_scan(direction):
         h = h.flip(1)
     h = h.reshape(batch, d, L).permute(0, 2, 1).numpy()
     assert_close(y, h, 1e-4, "S6 (N=1) vs linear scan")
+
+
+def test_s6_beyond_2_32_elements():
+    """A bidirectional bf16 scan of 2^21 + 5 steps over 2112 channels
+    (4.4e9 (b, t, d) elements, y above 16 GiB): 64-bit offsets everywhere, a
+    ragged last chunk and a partly filled last workgroup. Inputs drawn on the
+    GPU from a seeded generator with the pages' distributions; the float64
+    oracle runs the sampled channels in full."""
+    L, d_inner, N = (1 << 21) + 5, 2112, 16
+    say(f"s6 bidir bf16 (1, {L}, {d_inner}, {N}): {L * d_inner:.3e} elements")
+    dev = need_gpu()
+    g = torch.Generator(device=dev).manual_seed(4321)
+    u = torch.randn(1, L, d_inner, generator=g, device=dev).to(torch.bfloat16)
+    x = torch.randn(1, L, d_inner, generator=g, device=dev) * 0.5 - 1.0
+    delta = torch.nn.functional.softplus(x).to(torch.bfloat16)
+    del x
+    B = torch.randn(1, L, N, generator=g, device=dev).to(torch.bfloat16)
+    C = torch.randn(1, L, N, generator=g, device=dev).to(torch.bfloat16)
+    A = (-torch.arange(1, N + 1, dtype=torch.float32, device=dev)).expand(d_inner, N).contiguous()
+    D = torch.ones(d_inner, device=dev)
+    y = ssm.selective_scan_fwd(u, delta, A, B, C, D, direction="bidir")
+    torch.cuda.synchronize()
+    chans = [0, 63, 64, 1000, 2047, 2048, 2111]
+    got = y[0, :, chans].cpu().numpy()
+    del y
+    host = lambda t: t.float().cpu().numpy()
+    Bh, Ch = host(B), host(C)
+    worst = 0.0
+    for k, d in enumerate(chans):
+        ref, _ = native.selective_scan(host(u[:, :, d:d + 1]), host(delta[:, :, d:d + 1]),
+                                       host(A[d:d + 1]), Bh, Ch, host(D[d:d + 1]), "bidir")
+        err = max_scaled_err(got[:, k], ref[0, :, 0])
+        worst = max(worst, err)
+        say(f"  channel {d}: max |err|/(1+|ref|) = {err:.3e}")
+    assert worst <= TOL["bf16"]
 
 
 EDGE = [
