@@ -201,6 +201,27 @@ __device__ __forceinline__ float s6_step(float dt, float x, const Row<T, NT> &Br
 // side. The |y| half is written by the sweep that completes y (0 until
 // then); in a bidirectional call the reverse sweep also writes it into the
 // forward words of the same steps (16-bit stores) when the blocks line up.
+// Reads one element per 64 bytes of the B and C rows of one block of steps
+// (first_elem: element offset of the block's lowest row), lanes 0-31 in B and
+// 32-63 in C, so that those lines are on their way to L2 before the scalar
+// loads of the block ask for them. The value means nothing; holding it until
+// a later point (keep_alive) is what keeps the loads.
+template <typename T, int NT>
+__device__ __forceinline__ uint32_t touch_rows(const T *__restrict__ B, const T *__restrict__ C,
+                                               size_t first_elem) {
+  constexpr int kElems = kPrefetch * NT;
+  constexpr int kStride = 64 / int(sizeof(T));
+  const int lane = int(__lane_id());
+  const T *base = lane < 32 ? B : C;
+  const int i = min((lane & 31) * kStride, kElems - 1);
+  const T v = base[first_elem + size_t(i)];
+  if constexpr (sizeof(T) == 4)
+    return __float_as_uint(v);
+  else
+    return uint32_t(v);
+}
+__device__ __forceinline__ void keep_alive(uint32_t v) { asm volatile("" ::"v"(v)); }
+
 struct SweepStats {
   float *s_end;
   uint32_t *word;
@@ -247,7 +268,11 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
                            st.mirror + stat_index(g, b, c, full / kPrefetch - 1, d))
                      : nullptr;
   float rd[kPrefetch], rx[kPrefetch], ry[kPrefetch];
+  // Lowest row of the block of steps starting at sweep index i.
+  auto block_row = [&](int i) { return row0 + tof(Reverse ? i + kPrefetch - 1 : i); };
+  uint32_t touched = 0;
   if (full > 0) {
+    touched = touch_rows<T, NT>(B, C, block_row(0) * NT);
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       const size_t r = row(j);
@@ -264,6 +289,7 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
       cx[j] = rx[j];
       if (Accumulate) cy[j] = ry[j];
     }
+    keep_alive(touched);  // issued a block ago, with the loads just consumed
     if (i0 + kPrefetch < full) {
 #pragma unroll
       for (int j = 0; j < kPrefetch; ++j) {
@@ -272,6 +298,7 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
         rx[j] = ldv(&at(u + rn, io));
         if (Accumulate) ry[j] = at(y + rn, yo);
       }
+      touched = touch_rows<T, NT>(B, C, block_row(i0 + kPrefetch) * NT);
     }
     // B/C rows go one step ahead: step j's rows were loaded during step j-1.
     Row<T, NT> Bc, Cc;
@@ -639,7 +666,12 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   const FixGroups<NT> groups(Ap, cin);
   // Loads what block k needs into (dr, yr, s_in): its delta and y words and
   // the running sum before it.
-  auto load_block = [&](int k, float (&dr)[kPrefetch], float (&yr)[kPrefetch], float &s_in) {
+  // The loads also bring the block's C rows toward L2 (touched, held until
+  // the block runs), ahead of its scalar row loads.
+  auto load_block = [&](int k, float (&dr)[kPrefetch], float (&yr)[kPrefetch], float &s_in,
+                        uint32_t &touched) {
+    touched = touch_rows<T, NT>(
+        C, C, (row0 + tof(Reverse ? k * kPrefetch + kPrefetch - 1 : k * kPrefetch)) * NT);
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       dr[j] = ldv(&at(delta + row(k * kPrefetch + j), io));
@@ -649,7 +681,8 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   };
   // Evaluates block k from its loaded words for the groups in live.
   auto run_block = [&](int k, const float (&dr)[kPrefetch], const float (&yr)[kPrefetch],
-                       float S, uint32_t live) {
+                       float S, uint32_t live, uint32_t touched) {
+    keep_alive(touched);
     float Sj[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
@@ -698,14 +731,16 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
     // it computes.
     int i = __builtin_ctz(masks) / 4;
     float dr[kPrefetch], yr[kPrefetch], s_in;
-    load_block(w0 + i, dr, yr, s_in);
+    uint32_t tr;
+    load_block(w0 + i, dr, yr, s_in, tr);
     for (;;) {
       const uint32_t live = (masks >> (4 * i)) & 0xfu;
       masks &= ~(0xfu << (4 * i));
       const int inext = masks ? __builtin_ctz(masks) / 4 : -1;
       float dn[kPrefetch], yn[kPrefetch], sn = 0.0f;
-      if (inext >= 0) load_block(w0 + inext, dn, yn, sn);
-      run_block(w0 + i, dr, yr, s_in, live);
+      uint32_t tn = 0;
+      if (inext >= 0) load_block(w0 + inext, dn, yn, sn, tn);
+      run_block(w0 + i, dr, yr, s_in, live, tr);
       if (inext < 0) break;
       i = inext;
 #pragma unroll
@@ -714,6 +749,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
         yr[j] = yn[j];
       }
       s_in = sn;
+      tr = tn;
     }
   }
   float S = nfull > 0 ? s_end[s0 + size_t(nfull - 1) * ss] : 0.0f;
