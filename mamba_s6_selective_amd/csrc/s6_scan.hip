@@ -267,7 +267,12 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
                      ? reinterpret_cast<uint16_t *>(
                            st.mirror + stat_index(g, b, c, full / kPrefetch - 1, d))
                      : nullptr;
-  float rd[kPrefetch], rx[kPrefetch], ry[kPrefetch];
+  // Two register sets for a block's delta, u (and y) words: one feeds the
+  // block being computed while the next block's loads land in the other,
+  // and the loop runs two blocks per iteration so the sets trade roles
+  // without copies.
+  float ad[kPrefetch], ax[kPrefetch], ay[kPrefetch];
+  float bd[kPrefetch], bx[kPrefetch], by[kPrefetch];
   // Lowest row of the block of steps starting at sweep index i.
   auto block_row = [&](int i) { return row0 + tof(Reverse ? i + kPrefetch - 1 : i); };
   uint32_t touched = 0;
@@ -276,27 +281,28 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       const size_t r = row(j);
-      rd[j] = ldv(&at(delta + r, io));
-      rx[j] = ldv(&at(u + r, io));
-      if (Accumulate) ry[j] = at(y + r, yo);
+      ad[j] = ldv(&at(delta + r, io));
+      ax[j] = ldv(&at(u + r, io));
+      if (Accumulate) ay[j] = at(y + r, yo);
     }
   }
-  for (int i0 = 0; i0 < full; i0 += kPrefetch) {
-    float cd[kPrefetch], cx[kPrefetch], cy[kPrefetch];
+  // One block of kPrefetch steps from sweep index i0, its words in (rd, cx,
+  // cy); the next block's words are loaded into (nd, nx, ny).
+  auto block = [&](int i0, const float (&rd)[kPrefetch], const float (&cx)[kPrefetch],
+                   const float (&cy)[kPrefetch], float (&nd)[kPrefetch], float (&nx)[kPrefetch],
+                   float (&ny)[kPrefetch]) {
+    float cd[kPrefetch];
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
+    for (int j = 0; j < kPrefetch; ++j)
       cd[j] = dx(rd[j]);  // transformed when used: its load has had a block of steps to land
-      cx[j] = rx[j];
-      if (Accumulate) cy[j] = ry[j];
-    }
     keep_alive(touched);  // issued a block ago, with the loads just consumed
     if (i0 + kPrefetch < full) {
 #pragma unroll
       for (int j = 0; j < kPrefetch; ++j) {
         const size_t rn = row(i0 + kPrefetch + j);
-        rd[j] = ldv(&at(delta + rn, io));
-        rx[j] = ldv(&at(u + rn, io));
-        if (Accumulate) ry[j] = at(y + rn, yo);
+        nd[j] = ldv(&at(delta + rn, io));
+        nx[j] = ldv(&at(u + rn, io));
+        if (Accumulate) ny[j] = at(y + rn, yo);
       }
       touched = touch_rows<T, NT>(B, C, block_row(i0 + kPrefetch) * NT);
     }
@@ -339,6 +345,11 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
         pm -= 2 * ss;  // 2 halves per 32-bit word
       }
     }
+  };
+  for (int i0 = 0; i0 < full; i0 += 2 * kPrefetch) {
+    block(i0, ad, ax, ay, bd, bx, by);
+    if (i0 + kPrefetch >= full) break;
+    block(i0 + kPrefetch, bd, bx, by, ad, ax, ay);
   }
   for (int i = full; i < len; ++i) {
     const size_t r = row(i);
