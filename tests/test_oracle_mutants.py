@@ -153,7 +153,11 @@ def test_unmutated_copy_passes():
 
 @pytest.mark.parametrize("name", S6_MUTANTS)
 def test_s6_mutant_is_caught(name):
-    assert s6_pin_failures(_s6_mutant(name), oracle.linear_scan) != [], name
+    # some mutants (a flipped sign of A, u in the exponent) overflow; that is
+    # part of how they fail
+    with np.errstate(over="ignore", invalid="ignore"):
+        failures = s6_pin_failures(_s6_mutant(name), oracle.linear_scan)
+    assert failures != [], name
 
 
 # -------------------------------------------------------------- softplus ---
