@@ -91,6 +91,29 @@ def _dev_tensor(t, name, dtypes):
     return t
 
 
+def _same_device(**tensors):
+    """All given tensors (None skipped) on one device, and each output
+    (names starting with "out" or "h_last") sharing no memory with any input."""
+    items = [(k, t) for k, t in tensors.items() if t is not None]
+    dev = items[0][1].device
+    for k, t in items:
+        if t.device != dev:
+            raise ValueError(f"{k} is on {t.device}, expected {dev}")
+
+    def span(t):
+        start = t.data_ptr()
+        return start, start + t.numel() * t.element_size()
+
+    outs = [(k, t) for k, t in items if k.startswith("out") or k == "h_last"]
+    ins = [(k, t) for k, t in items if not (k.startswith("out") or k == "h_last")]
+    for ko, o in outs:
+        o0, o1 = span(o)
+        for ki, i in ins + [x for x in outs if x[0] != ko]:
+            i0, i1 = span(i)
+            if o0 < i1 and i0 < o1:
+                raise ValueError(f"{ko} overlaps {ki}")
+
+
 def _linear_args(a, b, out):
     import torch
     _dev_tensor(a, "a", (torch.float32,))
@@ -103,6 +126,7 @@ def _linear_args(a, b, out):
         _dev_tensor(out, "out", (torch.float32,))
         if out.shape != a.shape:
             raise ValueError("out must match a")
+    _same_device(a=a, b=b, out=out)
     return out
 
 
@@ -133,6 +157,7 @@ def linear_scan_batched(a, b, h0=None, out=None, h_last=None):
         _dev_tensor(h_last, "h_last", (torch.float32,))
         if h_last.shape != (nseq,):
             raise ValueError("h_last must have shape (nseq,)")
+    _same_device(a=a, b=b, h0=h0, out=out, h_last=h_last)
     with torch.cuda.device(a.device):
         _check(lib.ssm_linear_scan_batched(
             a.data_ptr(), b.data_ptr(), None if h0 is None else h0.data_ptr(), out.data_ptr(),
@@ -167,16 +192,7 @@ def linear_scan(a, b, h0: float = 0.0, out=None):
     """h[t] = a[t]*h[t-1] + b[t], h[-1] = h0 (fp32, 1-D device tensors)."""
     import torch
     lib = load_library()
-    _dev_tensor(a, "a", (torch.float32,))
-    _dev_tensor(b, "b", (torch.float32,))
-    if a.shape != b.shape or a.dim() != 1:
-        raise ValueError("a and b must be 1-D and of equal length")
-    if out is None:
-        out = torch.empty_like(a)
-    else:
-        _dev_tensor(out, "out", (torch.float32,))
-        if out.shape != a.shape:
-            raise ValueError("out must match a")
+    out = _linear_args(a, b, out)
     with torch.cuda.device(a.device):
         _check(lib.ssm_linear_scan(a.data_ptr(), b.data_ptr(), float(h0), out.data_ptr(),
                                    a.numel(), _stream(a)))
@@ -217,6 +233,7 @@ def selective_scan_fwd(u, delta, A, B, C, D, direction: str = "fwd", out=None,
         _dev_tensor(delta_bias, "delta_bias", (torch.float32,))
         if delta_bias.shape != (d,):
             raise ValueError("delta_bias must have shape (d,)")
+    _same_device(u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=delta_bias, out=out)
     if delta_softplus or delta_bias is not None:
         flags = (SSM_FLAG_BF16 if dt == torch.bfloat16 else 0) | \
             (SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0)
@@ -243,6 +260,7 @@ def copy_f32(src, dst):
     _dev_tensor(dst, "dst", (torch.float32,))
     if src.numel() != dst.numel():
         raise ValueError("src and dst sizes differ")
+    _same_device(src=src, out_dst=dst)
     with torch.cuda.device(src.device):
         _check(lib.ssm_copy_f32(src.data_ptr(), dst.data_ptr(), src.numel(), _stream(src)))
     return dst

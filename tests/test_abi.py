@@ -137,3 +137,19 @@ def test_selective_scan_ex_argument_errors():
     assert f(*no_bias, 0, 8, 4, 16, 0, ssm.SSM_FLAG_DELTA_SOFTPLUS, None) == ssm.SSM_OK
     mis = [FAKE, FAKE, FAKE_MISALIGNED] + [FAKE] * 5
     assert f(*mis, 1, 8, 4, 16, 0, ssm.SSM_FLAG_DELTA_SOFTPLUS, None) == ssm.SSM_ERR_INVALID_ARG
+
+
+def test_binding_rejects_overlapping_outputs():
+    """Outputs may not share memory with inputs (the kernels read inputs after
+    writing outputs); disjoint views of one buffer are fine."""
+    import torch
+    a, b = torch.zeros(16), torch.zeros(16)
+    ssm._same_device(a=a, b=b, out=torch.zeros(16))
+    ssm._same_device(a=a[:8], b=b, out=a[8:])
+    for out in (a, a[4:12], b[15:]):
+        with pytest.raises(ValueError):
+            ssm._same_device(a=a, b=b, out=out)
+    ssm._same_device(a=a, b=b, out=torch.zeros(4), h_last=torch.zeros(4))
+    h = torch.zeros(8)
+    with pytest.raises(ValueError):  # two outputs in one buffer
+        ssm._same_device(a=a, b=b, out=h, h_last=h[3:5])
