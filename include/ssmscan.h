@@ -6,7 +6,8 @@
  * library never frees or retains it past the call. Work is enqueued on
  * `stream` (a hipStream_t passed as void*; NULL means the default stream) and
  * the call returns without synchronising. Outputs are fully overwritten and
- * must not alias any input. Every pointer to data must be 16-byte aligned.
+ * must not overlap any input or each other (checked from the pointers and
+ * sizes: SSM_ERR_INVALID_ARG). Every pointer to data must be 16-byte aligned.
  *
  * Return codes (ssm_status_t): SSM_OK on success; on any error nothing is
  * launched and ssm_last_error() describes the cause (per calling thread).
@@ -72,7 +73,8 @@ typedef enum {
  * Uses a library-owned workspace cached per (device, stream); concurrent
  * calls on the same stream are ordered by the stream.
  * Errors: SSM_ERR_INVALID_ARG for n < 0, null or non-16-byte-aligned a, b, h
- * with n > 0; SSM_ERR_ALLOC / SSM_ERR_HIP on runtime failure.
+ * with n > 0, or h overlapping a or b; SSM_ERR_ALLOC / SSM_ERR_HIP on
+ * runtime failure.
  */
 SSM_API int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t n,
                             void *stream);
@@ -94,9 +96,10 @@ SSM_API int ssm_linear_scan(const float *a, const float *b, float h0, float *h, 
  * zero discards the state before it even when that state is inf or NaN (IEEE
  * arithmetic, and ssm_linear_scan, would give NaN); this is what keeps one
  * sequence's non-finite values out of the next.
- * Errors: SSM_ERR_INVALID_ARG for negative sizes or a null / misaligned a, b,
- * h with work to do; SSM_ERR_UNSUPPORTED for nseq * len > 2^31; nseq == 0 or
- * len == 0 is a no-op.
+ * Errors: SSM_ERR_INVALID_ARG for negative sizes, a null / misaligned a, b,
+ * h with work to do, or h / h_last overlapping an input or each other;
+ * SSM_ERR_UNSUPPORTED for nseq * len > 2^31; nseq == 0 or len == 0 is a
+ * no-op.
  */
 SSM_API int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, float *h,
                                     float *h_last, int64_t nseq, int64_t len, void *stream);
@@ -152,10 +155,10 @@ SSM_API int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *
  * y        : float[batch][L][d_inner], output (fp32).
  * direction: ssm_direction_t.
  * The (batch, L, d_inner, N) tensors dA, dBu and h never touch memory.
- * Errors: SSM_ERR_INVALID_ARG for negative sizes, a bad direction, or a
- * null / misaligned pointer with non-zero work; SSM_ERR_UNSUPPORTED for
- * N outside 1..16; zero batch, L or d_inner is a no-op returning SSM_OK
- * (checked after the direction and N).
+ * Errors: SSM_ERR_INVALID_ARG for negative sizes, a bad direction, a
+ * null / misaligned pointer with non-zero work, or y overlapping an input;
+ * SSM_ERR_UNSUPPORTED for N outside 1..16; zero batch, L or d_inner is a
+ * no-op returning SSM_OK (checked after the direction and N).
  */
 SSM_API int ssm_selective_scan_fwd(const float *u, const float *delta, const float *A,
                                    const float *B, const float *C, const float *D, float *y,
@@ -204,7 +207,7 @@ SSM_API int ssm_selective_scan_fwd_ex(const void *u, const void *delta, const fl
  * Device copy dst[i] = src[i], i < n (fp32). A known-simple streaming kernel
  * used by measurement code as the bandwidth reference and as the sentinel
  * that must reproduce its input exactly before a timing sweep counts.
- * Errors: as ssm_linear_scan.
+ * Errors: as ssm_linear_scan (dst overlapping src is an invalid argument).
  */
 SSM_API int ssm_copy_f32(const float *src, float *dst, int64_t n, void *stream);
 

@@ -21,6 +21,13 @@ thread_local std::string g_last_error;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The byte ranges [p, p + pb) and [q, q + qb) share memory (q may be null).
+bool overlap(const void *p, size_t pb, const void *q, size_t qb) {
+  if (!p || !q) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + qb && b < a + pb;
+}
+
 // Workspace of the look-back linear scan for one (device, stream): the tile
 // status words. Never reset between launches: each launch uses a fresh epoch.
 struct LinearWorkspace {
@@ -218,6 +225,9 @@ int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t 
   const int64_t ntiles = (n + tile - 1) / tile;
   if (ntiles > kLinearMaxTiles)
     return fail(SSM_ERR_UNSUPPORTED, "n too large for one launch (max 2^31 elements)");
+  const size_t bytes = size_t(n) * sizeof(float);
+  if (overlap(h, bytes, a, bytes) || overlap(h, bytes, b, bytes))
+    return fail(SSM_ERR_INVALID_ARG, "h overlaps a or b");
   LinearStatus status{};
   uint32_t epoch = 0;
   int grid = 0;
@@ -239,6 +249,12 @@ int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, flo
   if (nseq > (int64_t(1) << 31) / len)
     return fail(SSM_ERR_UNSUPPORTED, "nseq * len too large for one launch (max 2^31 elements)");
   const int64_t n = nseq * len;
+  const size_t bytes = size_t(n) * sizeof(float), sbytes = size_t(nseq) * sizeof(float);
+  if (overlap(h, bytes, a, bytes) || overlap(h, bytes, b, bytes) || overlap(h, bytes, h0, sbytes))
+    return fail(SSM_ERR_INVALID_ARG, "h overlaps a, b or h0");
+  if (overlap(h_last, sbytes, a, bytes) || overlap(h_last, sbytes, b, bytes) ||
+      overlap(h_last, sbytes, h, bytes) || overlap(h_last, sbytes, h0, sbytes))
+    return fail(SSM_ERR_INVALID_ARG, "h_last overlaps a, b, h or h0");
   const int64_t tile = linear_tile_elems(true);
   const int64_t ntiles = (n + tile - 1) / tile;
   LinearStatus status{};
@@ -260,6 +276,9 @@ static int linear_3pass_common(const float *a, const float *b, float h0, float *
   if (!aligned16(a) || !aligned16(b) || !aligned16(h))
     return fail(SSM_ERR_INVALID_ARG, "a, b and h must be 16-byte aligned");
   if (n > (int64_t(1) << 31)) return fail(SSM_ERR_UNSUPPORTED, "n too large (max 2^31 elements)");
+  const size_t bytes = size_t(n) * sizeof(float);
+  if (overlap(h, bytes, a, bytes) || overlap(h, bytes, b, bytes))
+    return fail(SSM_ERR_INVALID_ARG, "h overlaps a or b");
   hipStream_t s = static_cast<hipStream_t>(stream);
   void *ws = nullptr;
   if (int rc = scratch_workspace(s, linear3_workspace_bytes(n), &ws)) return rc;
@@ -284,13 +303,15 @@ int ssm_copy_f32(const float *src, float *dst, int64_t n, void *stream) {
   if (!src || !dst) return fail(SSM_ERR_INVALID_ARG, "null pointer with n > 0");
   if (!aligned16(src) || !aligned16(dst))
     return fail(SSM_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  if (overlap(dst, size_t(n) * sizeof(float), src, size_t(n) * sizeof(float)))
+    return fail(SSM_ERR_INVALID_ARG, "dst overlaps src");
   return hip_check(launch_copy_f32(src, dst, n, static_cast<hipStream_t>(stream)),
                    "copy launch");
 }
 
 static int s6_check(const void *u, const void *delta, const float *A, const void *B,
                     const void *C, const float *D, float *y, int batch, int L, int d_inner,
-                    int N, int direction, bool *noop) {
+                    int N, int direction, size_t esize, bool *noop) {
   *noop = false;
   if (batch < 0 || L < 0 || d_inner < 0 || N < 0)
     return fail(SSM_ERR_INVALID_ARG, "sizes must be >= 0");
@@ -309,6 +330,14 @@ static int s6_check(const void *u, const void *delta, const float *A, const void
     if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   if (int64_t(batch) * L * d_inner > (int64_t(1) << 40))
     return fail(SSM_ERR_UNSUPPORTED, "problem too large");
+  const size_t e = size_t(batch) * size_t(L) * size_t(d_inner);  // (b, t, d) elements
+  const size_t r = size_t(batch) * size_t(L) * size_t(N);        // (b, t, n) elements
+  const size_t yb = e * sizeof(float);
+  if (overlap(y, yb, u, e * esize) || overlap(y, yb, delta, e * esize) ||
+      overlap(y, yb, B, r * esize) || overlap(y, yb, C, r * esize) ||
+      overlap(y, yb, A, size_t(d_inner) * N * sizeof(float)) ||
+      overlap(y, yb, D, size_t(d_inner) * sizeof(float)))
+    return fail(SSM_ERR_INVALID_ARG, "y overlaps an input");
   return SSM_OK;
 }
 
@@ -318,7 +347,7 @@ int ssm_selective_scan_fwd(const float *u, const float *delta, const float *A,
                            void *stream) {
   g_last_error.clear();
   bool noop = false;
-  if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, &noop))
+  if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, 4, &noop))
     return rc;
   if (noop) return SSM_OK;
   S6Args args{u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, false, false, nullptr};
@@ -331,7 +360,7 @@ int ssm_selective_scan_fwd_bf16(const uint16_t *u, const uint16_t *delta, const 
                                 int direction, void *stream) {
   g_last_error.clear();
   bool noop = false;
-  if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, &noop))
+  if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, 2, &noop))
     return rc;
   if (noop) return SSM_OK;
   S6Args args{u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, true, false, nullptr};
@@ -349,11 +378,15 @@ int ssm_selective_scan_fwd_ex(const void *u, const void *delta, const float *del
   if (delta_bias && !softplus)
     return fail(SSM_ERR_INVALID_ARG, "delta_bias is only applied with SSM_FLAG_DELTA_SOFTPLUS");
   bool noop = false;
-  if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, &noop))
+  const size_t esize = (flags & SSM_FLAG_BF16) ? 2 : 4;
+  if (int rc = s6_check(u, delta, A, B, C, D, y, batch, L, d_inner, N, direction, esize, &noop))
     return rc;
   if (noop) return SSM_OK;
   if (delta_bias && !aligned16(delta_bias))
     return fail(SSM_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (overlap(y, size_t(batch) * size_t(L) * size_t(d_inner) * sizeof(float), delta_bias,
+              size_t(d_inner) * sizeof(float)))
+    return fail(SSM_ERR_INVALID_ARG, "y overlaps an input");
   S6Args args{u,     delta,    A, B, C, D, y, batch, L, d_inner, N, direction,
               (flags & SSM_FLAG_BF16) != 0, softplus, delta_bias};
   return run_s6(args, static_cast<hipStream_t>(stream));

@@ -153,3 +153,26 @@ def test_binding_rejects_overlapping_outputs():
     h = torch.zeros(8)
     with pytest.raises(ValueError):  # two outputs in one buffer
         ssm._same_device(a=a, b=b, out=h, h_last=h[3:5])
+
+
+def test_outputs_overlapping_inputs_are_rejected():
+    """The library checks output ranges against input ranges from the
+    pointers and sizes, before any HIP call (nothing is dereferenced)."""
+    lib = ssm.load_library()
+    A, B = 0x100000, 0x200000   # 1 MiB apart
+    # linear: h = a, h inside b, h just past the end of a (fine)
+    assert lib.ssm_linear_scan(A, B, 0.0, A, 16, None) == ssm.SSM_ERR_INVALID_ARG
+    assert b"overlaps" in lib.ssm_last_error()
+    assert lib.ssm_linear_scan(A, B, 0.0, B + 16, 16, None) == ssm.SSM_ERR_INVALID_ARG
+    assert lib.ssm_linear_scan_3pass(A, B, 0.0, A + 48, 16, None) == ssm.SSM_ERR_INVALID_ARG
+    assert lib.ssm_copy_f32(A, A + 32, 16, None) == ssm.SSM_ERR_INVALID_ARG
+    # batched: h_last inside h
+    assert lib.ssm_linear_scan_batched(A, B, None, 0x300000, 0x300000 + 64, 4, 8, None) == \
+        ssm.SSM_ERR_INVALID_ARG
+    # S6: y on top of B (bf16 B is smaller than the fp32 y)
+    P = [0x1000000 * (k + 1) for k in range(7)]
+    bad = list(P)
+    bad[6] = P[3] + 32
+    for fn in (lib.ssm_selective_scan_fwd, lib.ssm_selective_scan_fwd_bf16):
+        assert fn(*bad, 1, 10, 8, 16, 0, None) == ssm.SSM_ERR_INVALID_ARG
+        assert b"overlaps" in lib.ssm_last_error()
