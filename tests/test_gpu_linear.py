@@ -128,14 +128,15 @@ def test_linear_homogeneous_bit_exact_full_size():
     assert bad == 0
 
 
-def test_linear_maximum_size_carry_exact():
+@pytest.mark.parametrize("n", [1 << 31, (1 << 31) - 4093])
+def test_linear_maximum_size_carry_exact(n):
     """n = 2^31, the largest length the single-pass scan accepts (every
-    look-back level full: 64 blocks of 64 superblocks of 64 tiles), with
-    a = 1 and b = 1 at 1000 seeded positions, 0 elsewhere: every carry crosses
-    the whole sequence, and h[i] = h0 + (number of ones at positions <= i)
-    exactly in fp32 whatever the grouping. Checked at every tile's last
-    element, at the ones and just before them, and at 2^20 seeded positions."""
-    n = 1 << 31
+    look-back level full: 64 blocks of 64 superblocks of 64 tiles), and the
+    same with a ragged last tile, with a = 1 and b = 1 at 1000 seeded
+    positions, 0 elsewhere: every carry crosses the whole sequence, and
+    h[i] = h0 + (number of ones at positions <= i) exactly in fp32 whatever
+    the grouping. Checked at every tile's last element, at the ones and just
+    before them, at the last element and at 2^20 seeded positions."""
     say(f"linear maximum size n={n}: a = 1, sparse integer b")
     dev = need_gpu()
     g = torch.Generator().manual_seed(2031)
