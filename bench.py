@@ -62,6 +62,19 @@ def load_traffic(kind, *kernel_srcs):
 SETTLE = {"s": 1.0}
 
 
+def load_s6_traffic(name):
+    """HBM bytes of one S6 call (chunk + carry + fix passes) on workload `name`
+    from committed rocprofv3 counter summaries, or None if absent or taken on
+    a different kernel source."""
+    f = PROFILES / "s6_traffic.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text()).get(name)
+    if not d or d.get("kernel_source_sha") != source_hash("s6_scan.hip", "s6_internal.h"):
+        return None
+    return d.get("bytes_per_launch")
+
+
 def time_steps(fn, steps, warmup):
     """Runs fn() warmup times (and on, untimed, until SETTLE["s"] seconds have
     passed, so that the clocks have settled), then `steps` timed times
@@ -235,7 +248,7 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
         "roofline": {"bound": "alu", "achieved": round(lane_cycles / (ms_kernel * 1e-3) / 1e12, 3),
                      "peak": round(VALU_PEAK_T, 2), "unit": "T lane-cycles/s",
                      "frac": round(alu_frac, 4), "exp_cost_lane_cycles": exp_cost,
-                     "traffic": None},
+                     "traffic": load_s6_traffic(name)},
         "hbm": {"achieved_GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4),
                 "algorithmic_bytes": nbytes},
         "fused_softplus": fused,

@@ -11,10 +11,11 @@
         --kernel linear_scan_kernel --copy-bytes 1073741824 \\
         --source linear_scan.hip scan_common.h \\
         --out profiles/linear_scan_traffic.json
-        HBM bytes per launch of a kernel from two counter runs (FETCH_SIZE, then
-        WRITE_SIZE, both in KiB per dispatch), each scaled by the ratio of the
-        bytes the copy kernel moves (copy_bytes read, copy_bytes written) to
-        what the same counter reads for it.
+        HBM bytes per launch of a kernel (or summed over several kernels, one
+        dispatch each: the passes of one call) from two counter runs
+        (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled by
+        the ratio of the bytes the copy kernel moves (copy_bytes read,
+        copy_bytes written) to what the same counter reads for it.
 """
 from __future__ import annotations
 
@@ -95,14 +96,15 @@ def pick(d, key):
 def cmd_traffic(args):
     fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE")
     write = counter_per_dispatch(args.write, "WRITE_SIZE")
-    kf = statistics.median(pick(fetch, args.kernel))
-    kw = statistics.median(pick(write, args.kernel))
+    # one kernel, or the sum over the kernels of one step
+    kf = sum(statistics.median(pick(fetch, k)) for k in args.kernel)
+    kw = sum(statistics.median(pick(write, k)) for k in args.kernel)
     cf = statistics.median(pick(fetch, COPY_KERNEL))
     cw = statistics.median(pick(write, COPY_KERNEL))
     f_scale = args.copy_bytes / (cf * 1024.0)
     w_scale = args.copy_bytes / (cw * 1024.0)
     rec = {
-        "kernel": args.kernel,
+        "kernel": args.kernel[0] if len(args.kernel) == 1 else args.kernel,
         "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
         "copy_bytes": args.copy_bytes,
         "copy_fetch_kib": cf, "copy_write_kib": cw,
@@ -127,7 +129,8 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, nargs="+",
+                   help="kernel name (substring); several: bytes summed over one dispatch of each")
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--source", required=True, nargs="+",
                    help="csrc files the kernel is built from (hashed in this order)")
