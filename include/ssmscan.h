@@ -71,7 +71,10 @@ typedef enum {
  * the same left-to-right order). It is not bitwise equal to a sequential fp32
  * loop: partial products are associated differently.
  * Uses a library-owned workspace cached per (device, stream); concurrent
- * calls on the same stream are ordered by the stream.
+ * calls on the same stream are ordered by the stream. Each call hands its
+ * kernel a fresh epoch for the status words, so a call recorded in a HIP
+ * graph must not be replayed (a replay would reuse the epoch and read the
+ * previous replay's words); the same holds for ssm_linear_scan_batched.
  * Errors: SSM_ERR_INVALID_ARG for n < 0, null or non-16-byte-aligned a, b, h
  * with n > 0, or h overlapping a or b; SSM_ERR_ALLOC / SSM_ERR_HIP on
  * runtime failure.
