@@ -406,26 +406,34 @@ const char *ssm_status_string(int code) {
 const char *ssm_last_error(void) { return g_last_error.c_str(); }
 
 int ssm_release_workspace(void) {
+  g_last_error.clear();
   std::lock_guard<std::mutex> lock(g_mu);
   int rc = SSM_OK;
   int saved = 0;
   (void)hipGetDevice(&saved);
+  // Wait for every device that owns a workspace (not for its streams: a
+  // stream the caller has destroyed since would be an invalid handle).
+  std::map<int, bool> devices;
+  for (auto &kv : g_linear) devices[kv.first.first] = true;
+  for (auto &kv : g_s6) devices[kv.first.first] = true;
+  for (auto &kv : g_scratch) devices[kv.first.first] = true;
+  for (auto &dv : devices) {
+    if (hipSetDevice(dv.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+      rc = fail(SSM_ERR_HIP, "hipDeviceSynchronize failed while releasing workspaces");
+  }
   for (auto &kv : g_linear) {
     if (!kv.second.words) continue;
     (void)hipSetDevice(kv.first.first);
-    if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = SSM_ERR_HIP;
     (void)hipFree(kv.second.words);
   }
   for (auto &kv : g_s6) {
     if (!kv.second.buf) continue;
     (void)hipSetDevice(kv.first.first);
-    if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = SSM_ERR_HIP;
     (void)hipFree(kv.second.buf);
   }
   for (auto &kv : g_scratch) {
     if (!kv.second.buf) continue;
     (void)hipSetDevice(kv.first.first);
-    if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = SSM_ERR_HIP;
     (void)hipFree(kv.second.buf);
   }
   g_linear.clear();

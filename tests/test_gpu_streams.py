@@ -54,3 +54,24 @@ def test_s6_scans_on_two_streams_match_serial():
     for ys in outs:
         for y, ref in zip(ys, refs):
             assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
+
+
+def test_calls_after_release_workspace():
+    """ssm_release_workspace frees every cached workspace (after waiting for
+    the work that uses it); later calls allocate afresh and give the same
+    results bit for bit."""
+    dev = need_gpu()
+    say("calls after releasing the workspaces")
+    a, b = (t.to(dev) for t in linear_inputs(300001, seed=31, a_lo=0.5, a_hi=1.0))
+    inp = s6_inputs(2, 2000, 128, 16, seed=32, dtype="bf16")
+    t6 = [x.to(dev) for x in (inp.u, inp.delta, inp.A, inp.B, inp.C, inp.D)]
+    h_ref = ssm.linear_scan(a, b, 1.0)
+    y_ref = ssm.selective_scan_fwd(*t6, direction="bidir")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        ssm.release_workspace()
+        h = ssm.linear_scan(a, b, 1.0)
+        y = ssm.selective_scan_fwd(*t6, direction="bidir")
+        torch.cuda.synchronize()
+        assert torch.equal(h.view(torch.int32), h_ref.view(torch.int32))
+        assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
