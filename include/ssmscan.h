@@ -158,6 +158,10 @@ SSM_API int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *
  * y        : float[batch][L][d_inner], output (fp32).
  * direction: ssm_direction_t.
  * The (batch, L, d_inner, N) tensors dA, dBu and h never touch memory.
+ * Once a call on `stream` has sized that stream's workspace, a call with the
+ * same or smaller sizes only enqueues kernels (no allocation, no memset), so
+ * it may be recorded in a HIP graph and replayed (also for the _bf16 and _ex
+ * forms).
  * Errors: SSM_ERR_INVALID_ARG for negative sizes, a bad direction, a
  * null / misaligned pointer with non-zero work, or y overlapping an input;
  * SSM_ERR_UNSUPPORTED for N outside 1..16; zero batch, L or d_inner is a
