@@ -27,8 +27,8 @@ struct S6Args {
 int run_s6(const S6Args &args, hipStream_t stream);
 
 // Cached S6 workspace for (current device, stream), at least `bytes` long.
-// `tickets`, `ticket` and `epoch` serve kernels that order work with a ticket.
-int s6_workspace(hipStream_t stream, size_t bytes, int64_t tickets, void **buf,
-                 unsigned long long **ticket, unsigned long long *base, uint32_t *epoch);
+// Allocated (and zeroed) only when it grows; otherwise the call touches no
+// memory, so S6 calls that fit the workspace enqueue kernels only.
+int s6_workspace(hipStream_t stream, size_t bytes, void **buf);
 
 }  // namespace ssm

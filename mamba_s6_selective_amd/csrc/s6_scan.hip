@@ -879,10 +879,7 @@ int launch_all(const S6Args &a, hipStream_t stream) {
     const size_t sums = (size_t(a.batch) * g.nchunks * a.d_inner + 63) / 64 * 64;
     const size_t stats = (size_t(a.batch) * g.nchunks * g.nblk * a.d_inner + 63) / 64 * 64;
     void *buf = nullptr;
-    unsigned long long *ticket = nullptr, base = 0;
-    uint32_t epoch = 0;
-    if (int rc = s6_workspace(stream, (4 * per + sums + 4 * stats) * sizeof(float), 0, &buf,
-                              &ticket, &base, &epoch))
+    if (int rc = s6_workspace(stream, (4 * per + sums + 4 * stats) * sizeof(float), &buf))
       return rc;
     float *f = static_cast<float *>(buf);
     agg_s = f;

@@ -39,9 +39,6 @@ struct LinearWorkspace {
 struct S6Workspace {
   void *buf = nullptr;
   size_t bytes = 0;
-  unsigned long long *ticket = nullptr;
-  unsigned long long ticket_next = 0;
-  uint32_t epoch = 0;
 };
 
 // Plain scratch memory for one (device, stream), grown on demand.
@@ -139,14 +136,14 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
   return SSM_OK;
 }
 
-int s6_workspace(hipStream_t stream, size_t bytes, int64_t tickets, void **buf,
-                 unsigned long long **ticket, unsigned long long *base, uint32_t *epoch) {
+int s6_workspace(hipStream_t stream, size_t bytes, void **buf) {
   int dev = 0;
   if (int rc = current_device(&dev)) return rc;
   std::lock_guard<std::mutex> lock(g_mu);
   S6Workspace &ws = g_s6[Key(dev, stream)];
   if (ws.bytes < bytes || ws.buf == nullptr) {
     if (ws.buf) {
+      // The old buffer may still be read by launches queued on this stream.
       if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
       (void)hipFree(ws.buf);
       ws.buf = nullptr;
@@ -155,28 +152,16 @@ int s6_workspace(hipStream_t stream, size_t bytes, int64_t tickets, void **buf,
     size_t cap = 1 << 20;
     while (cap < bytes) cap *= 2;
     void *p = nullptr;
-    if (hipMalloc(&p, cap + 256) != hipSuccess)
+    if (hipMalloc(&p, cap) != hipSuccess)
       return fail(SSM_ERR_ALLOC, "hipMalloc of the S6 workspace failed");
-    if (int rc = hip_check(hipMemsetAsync(p, 0, cap + 256, stream), "hipMemsetAsync")) {
+    if (int rc = hip_check(hipMemsetAsync(p, 0, cap, stream), "hipMemsetAsync")) {
       (void)hipFree(p);
       return rc;
     }
     ws.buf = p;
     ws.bytes = cap;
-    ws.ticket = reinterpret_cast<unsigned long long *>(static_cast<char *>(p) + cap);
-    ws.ticket_next = 0;
   }
-  if (ws.epoch == 0xffffffffu) {
-    if (int rc = hip_check(hipMemsetAsync(ws.buf, 0, ws.bytes, stream), "hipMemsetAsync"))
-      return rc;
-    ws.epoch = 0;
-  }
-  ws.epoch += 1;
   *buf = ws.buf;
-  *ticket = ws.ticket;
-  *base = ws.ticket_next;
-  *epoch = ws.epoch;
-  ws.ticket_next += (unsigned long long)tickets;
   return SSM_OK;
 }
 
