@@ -70,11 +70,18 @@ typedef enum {
  * bitwise identical from run to run (the cross-tile carry is always folded in
  * the same left-to-right order). It is not bitwise equal to a sequential fp32
  * loop: partial products are associated differently.
- * Uses a library-owned workspace cached per (device, stream); concurrent
- * calls on the same stream are ordered by the stream. Each call hands its
- * kernel a fresh epoch for the status words, so a call recorded in a HIP
- * graph must not be replayed (a replay would reuse the epoch and read the
- * previous replay's words); the same holds for ssm_linear_scan_batched.
+ * Uses a library-owned workspace cached per (device, stream): counters and
+ * epoch-tagged status words that every launch leaves ready for the next, the
+ * epoch advancing on the device. So once a call on `stream` has sized that
+ * stream's workspace, a call of the same or smaller size only enqueues one
+ * kernel and may be recorded in a HIP graph and replayed (the same holds for
+ * ssm_linear_scan_batched). Launches on one workspace must not overlap: calls
+ * on one stream are ordered by it, and replays of a recorded call must be
+ * ordered with each other and with calls on the stream it was recorded on
+ * (overlapping launches can corrupt the counters and leave a later launch
+ * waiting forever). A call that would create or grow the workspace during
+ * capture fails with SSM_ERR_INVALID_ARG; a graph must not outlive its
+ * workspace (ssm_release_workspace, or a larger call on that stream, frees it).
  * Errors: SSM_ERR_INVALID_ARG for n < 0, null or non-16-byte-aligned a, b, h
  * with n > 0, or h overlapping a or b; SSM_ERR_ALLOC / SSM_ERR_HIP on
  * runtime failure.
@@ -161,7 +168,10 @@ SSM_API int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *
  * Once a call on `stream` has sized that stream's workspace, a call with the
  * same or smaller sizes only enqueues kernels (no allocation, no memset), so
  * it may be recorded in a HIP graph and replayed (also for the _bf16 and _ex
- * forms).
+ * forms); replays and calls on that stream must not overlap (they share the
+ * workspace). A call that would create or grow the workspace during capture
+ * fails with SSM_ERR_INVALID_ARG; a graph must not outlive its workspace
+ * (ssm_release_workspace, or a larger call on that stream, frees it).
  * Errors: SSM_ERR_INVALID_ARG for negative sizes, a bad direction, a
  * null / misaligned pointer with non-zero work, or y overlapping an input;
  * SSM_ERR_UNSUPPORTED for N outside 1..16; zero batch, L or d_inner is a
@@ -227,6 +237,18 @@ SSM_API const char *ssm_last_error(void);
 /* Frees every cached workspace after synchronising the device(s) that own
  * them. Safe to call at any time from a thread with no call in flight. */
 SSM_API int ssm_release_workspace(void);
+
+/*
+ * Diagnostic. The single-pass scans tag their status words with a 32-bit
+ * epoch taken from the device; after `cycle` launches on one workspace (by
+ * default 2^32 - 1, all non-zero tags) the epochs start again at 1, and the
+ * launch that ends a cycle clears every status word first. This sets the
+ * cycle for workspaces created afterwards, so that the clearing can be
+ * exercised with few calls; results do not depend on it.
+ * Errors: SSM_ERR_INVALID_ARG for cycle == 0 or while a linear-scan workspace
+ * exists (call ssm_release_workspace first).
+ */
+SSM_API int ssm_linear_scan_set_epoch_cycle(uint32_t cycle);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,16 @@ struct LinearStatus {
   AggWord *lvl0;
   AggWord *lvl1;
   AggWord *lvl2;
-  unsigned long long *ticket;  // two counters; launch e claims from ticket[e & 1]
+  // ((epoch - 1) << 32) | tiles claimed so far by the launch in progress; the
+  // launch's last claim stores the next launch's value. The epoch thus lives
+  // on the device, and a launch replayed from a recorded graph still gets a
+  // fresh one.
+  // claims[kDoneOffset] counts the waves that have finished, only in a
+  // launch that ends the epoch cycle.
+  unsigned long long *claims;
+  int64_t nwords;        // 64-bit words from lvl0 through lvl2 (padding included)
+  uint32_t epoch_cycle;  // epochs run 1 .. epoch_cycle, then start again at 1
+  static constexpr int kDoneOffset = 16;  // 128 bytes: its own cache line
 };
 
 // Largest tile count one launch supports (three levels of 64).
@@ -42,14 +51,16 @@ constexpr int64_t kLinearMaxTiles = int64_t(64) * 64 * 64;
 int64_t linear_tile_elems(bool segmented);
 
 // Enqueues the single-pass scan on min(ntiles, resident_wgs) persistent
-// workgroups. The status levels must hold ntiles, ceil(ntiles/64) and
-// ceil(ntiles/4096) entries whose epochs differ from `epoch`, and
-// ticket[epoch & 1] must be zero. seg_len > 0 scans n / seg_len independent
-// sequences of seg_len elements (sequence k from seg_h0[k], or 0 if seg_h0 is
+// workgroups (ntiles >= 1). The status levels must hold ntiles,
+// ceil(ntiles/64) and ceil(ntiles/4096) entries whose epochs differ from the
+// one *claims gives, *claims' count and *done must be 0 and *claims' epoch
+// below epoch_cycle: a zeroed workspace is so, and every launch leaves it so
+// for the next. Launches on one workspace must not overlap. seg_len > 0 scans
+// n / seg_len independent sequences of seg_len elements (sequence k from seg_h0[k], or 0 if seg_h0 is
 // null; its last value to seg_h_last[k] if that is not null); h0 is then
 // unused. n < 2^32 with segments.
 hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h,
-                              int64_t n, int64_t ntiles, LinearStatus status, uint32_t epoch,
+                              int64_t n, int64_t ntiles, LinearStatus status,
                               int resident_wgs, const float *seg_h0, float *seg_h_last,
                               uint32_t seg_len, hipStream_t stream);
 // Workgroups of the scan kernel that fit on one CU at once (0 on error).

@@ -409,29 +409,57 @@ __device__ __forceinline__ void tile_apply(const float4 (&va)[kRows], const floa
   }
 }
 
-constexpr int kClaimTiles = 1;  // consecutive tiles taken per ticket (see the kernel comment)
-
-__device__ __forceinline__ int64_t claim_batch(unsigned long long *ticket, int lane) {
-  unsigned long long t = 0;
-  if (lane == 0)
-    t = __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(t));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(t >> 32));
-  return int64_t((uint64_t(hi) << 32) | lo);
+// One claim on the launch's claims word, ((epoch - 1) << 32) | claims made so
+// far: the claimed tile (ntiles or more means none) and the launch's epoch.
+// Every workgroup claims one tile at a time until its first failed claim, so
+// a launch makes exactly ntiles + gridDim.x claims; the last of them hands
+// the next epoch (count 0) to the next launch on the workspace.
+struct Claim {
+  int64_t tile;
+  uint32_t epoch;
+};
+__device__ __forceinline__ Claim claim_tile(const LinearStatus &st, int64_t ntiles, int lane) {
+  unsigned long long w = 0;
+  if (lane == 0) {
+    w = __hip_atomic_fetch_add(st.claims, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (uint32_t(w) == uint32_t(ntiles) + gridDim.x - 1u) {
+      const uint32_t hi = uint32_t(w >> 32);
+      const uint32_t next = hi + 1u >= st.epoch_cycle ? 0u : hi + 1u;
+      __hip_atomic_store(st.claims, (unsigned long long)next << 32, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const uint32_t count = __builtin_amdgcn_readfirstlane(uint32_t(w));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(w >> 32));
+  return {count < ntiles ? int64_t(count) : ntiles, hi + 1u};
 }
 
-// The tile a workgroup scans after tile t: the next tile of its claimed batch,
-// or the first tile of a newly claimed batch. ntiles means "none".
-__device__ __forceinline__ int64_t successor(int64_t t, int64_t ntiles,
-                                             unsigned long long *ticket, int lane) {
+// The tile a workgroup scans after tile t (t < 0: its first), claimed anew;
+// ntiles means none, and a workgroup claims nothing after a failed claim.
+__device__ __forceinline__ int64_t successor(int64_t t, int64_t ntiles, const LinearStatus &st,
+                                             int lane) {
   if (t >= ntiles) return ntiles;
-  if (t < 0) {  // nothing claimed yet
-    const int64_t first = claim_batch(ticket, lane) * kClaimTiles;
-    return first < ntiles ? first : ntiles;
-  }
-  if ((t + 1) % kClaimTiles != 0) return t + 1 < ntiles ? t + 1 : ntiles;
-  const int64_t first = claim_batch(ticket, lane) * kClaimTiles;
-  return first < ntiles ? first : ntiles;
+  return claim_tile(st, ntiles, lane).tile;
+}
+
+// Called by every wave as it finishes. Epochs are 32-bit, so after a full
+// cycle a status word left from the previous pass over the epochs could look
+// current; the launch that takes the cycle's last epoch therefore counts its
+// waves out (acquire-release, so every status access of the launch comes
+// before), and the last wave out clears every status word (epoch 0, never
+// current) for the next cycle.
+__device__ __forceinline__ void check_out(const LinearStatus &st, uint32_t epoch, int lane) {
+  if (epoch < st.epoch_cycle) return;
+  unsigned long long *done = st.claims + LinearStatus::kDoneOffset;
+  unsigned long long d = 0;
+  if (lane == 0)
+    d = __hip_atomic_fetch_add(done, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t waves = uint32_t(gridDim.x) * (blockDim.x / 64u);
+  if (__builtin_amdgcn_readfirstlane(uint32_t(d)) != waves - 1u) return;
+  uint64_t *words = reinterpret_cast<uint64_t *>(st.lvl0);  // the levels lie back to back
+  for (int64_t i = lane; i < st.nwords; i += 64)
+    __hip_atomic_store(words + i, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) __hip_atomic_store(done, 0ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // LDS shared by the waves of one workgroup. Per-tile values are kept in
@@ -449,6 +477,7 @@ struct Shared {
   float carry[4][kWaves];                      // h entering each wave's rows
   int64_t ids[4];                              // claimed tiles, in claim order
   unsigned arrived[2];                         // data waves done with a tile's local scan
+  uint32_t epoch;                              // this launch's epoch
 };
 
 template <bool Seg, int kRows = Shape<Seg>::kRows>
@@ -539,35 +568,33 @@ __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
 // levels after the look-back of a lower tile), and a workgroup only waits on
 // tiles lower than the ones it owns; so the lowest unfinished tile can always
 // finish, however many workgroups the device keeps resident.
-// The ticket of a launch is st.ticket[epoch & 1]; the first workgroup zeroes
-// the other slot for the next launch on the stream.
+// The launch's epoch arrives with every claim (see claim_tile), so a launch
+// recorded in a HIP graph gets a fresh epoch on every replay.
 template <bool Seg>
 __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
     const float *__restrict__ a, const float *__restrict__ b, float h0,
-    float *__restrict__ h, int64_t n, int64_t ntiles, LinearStatus st, uint32_t epoch,
-    Segments sg) {
+    float *__restrict__ h, int64_t n, int64_t ntiles, LinearStatus st, Segments sg) {
   using Op = typename std::conditional<Seg, ResetOp, PlainOp>::type;
   constexpr int kWaves = Shape<Seg>::kWaves, kRows = Shape<Seg>::kRows;
   __shared__ Shared<Seg> sh;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  unsigned long long *ticket = st.ticket + (epoch & 1u);
 
   if (wave == kWaves) {
-    if (blockIdx.x == 0 && lane == 0)
-      __hip_atomic_store(st.ticket + ((epoch + 1u) & 1u), 0ull, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    const int64_t t0 = successor(-1, ntiles, ticket, lane);
-    const int64_t t1 = successor(t0, ntiles, ticket, lane);
-    const int64_t t2 = successor(t1, ntiles, ticket, lane);
+    const Claim first = claim_tile(st, ntiles, lane);
+    const uint32_t epoch = first.epoch;
+    const int64_t t0 = first.tile;
+    const int64_t t1 = successor(t0, ntiles, st, lane);
+    const int64_t t2 = successor(t1, ntiles, st, lane);
     if (lane == 0) {
       sh.ids[0] = t0;
       sh.ids[1] = t1;
       sh.ids[2] = t2;
       sh.arrived[0] = 0;
       sh.arrived[1] = 0;
+      sh.epoch = epoch;
     }
-    __syncthreads();  // A: first claims visible
+    __syncthreads();  // A: first claims and the epoch visible
     __syncthreads();  // B: t_0 scanned and published
     // Look-backs of t_{j-1} (lp) and t_j (ln). t_j's first status reads are
     // issued at the end of iteration j and read at the start of iteration j+1,
@@ -611,10 +638,12 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
       step(l1, l0);
       if (tp >= ntiles) break;
     }
+    check_out(st, epoch, lane);
     return;
   }
 
   __syncthreads();  // A
+  const uint32_t epoch = sh.epoch;
   int64_t tp = ntiles, t0 = sh.ids[0], t1 = sh.ids[1], t2 = sh.ids[2];
   // Register stages: (va, vb) tile being applied, (na, nb) tile being
   // scanned, (ma, mb) tile being loaded; prefixes of the two parked tiles.
@@ -630,7 +659,7 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
   // In iteration j: tp = t_{j-1}, t0 = t_j, t1 = t_{j+1}, t2 = t_{j+2}.
   for (int j = 0; j == 0 || tp < ntiles; ++j) {
     int64_t claimed = ntiles;
-    if (wave == 0 && t2 < ntiles) claimed = successor(t2, ntiles, ticket, lane);
+    if (wave == 0 && t2 < ntiles) claimed = successor(t2, ntiles, st, lane);
     float4 ma[kRows], mb[kRows];
     if (t2 < ntiles) load_tile<Seg>(a, b, n, t2, sg, ma, mb);
     float nia[kRows], nib[kRows];
@@ -657,6 +686,7 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
     t1 = t2;
     t2 = sh.ids[(j + 3) & 3];
   }
+  check_out(st, epoch, lane);
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const float *__restrict__ src,
@@ -676,7 +706,7 @@ int64_t linear_tile_elems(bool segmented) {
 }
 
 hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h,
-                              int64_t n, int64_t ntiles, LinearStatus status, uint32_t epoch,
+                              int64_t n, int64_t ntiles, LinearStatus status,
                               int resident_wgs, const float *seg_h0, float *seg_h_last,
                               uint32_t seg_len, hipStream_t stream) {
   const unsigned grid = unsigned(ntiles < resident_wgs ? ntiles : resident_wgs);
@@ -691,11 +721,11 @@ hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h
   if (seg_len == 0)
     hipLaunchKernelGGL(linear_scan_kernel<false>, dim3(grid), dim3(Shape<false>::kThreads + 64), 0,
                        stream, a,
-                       b, h0, h, n, ntiles, status, epoch, sg);
+                       b, h0, h, n, ntiles, status, sg);
   else
     hipLaunchKernelGGL(linear_scan_kernel<true>, dim3(grid), dim3(Shape<true>::kThreads + 64), 0,
                        stream, a,
-                       b, h0, h, n, ntiles, status, epoch, sg);
+                       b, h0, h, n, ntiles, status, sg);
   return hipGetLastError();
 }
 

@@ -28,13 +28,20 @@ bool overlap(const void *p, size_t pb, const void *q, size_t qb) {
   return a < b + qb && b < a + pb;
 }
 
-// Workspace of the look-back linear scan for one (device, stream): the tile
-// status words. Never reset between launches: each launch uses a fresh epoch.
+// Workspace of the look-back linear scan for one (device, stream): the
+// claims word, the wave count of a cycle's last launch and the tile status
+// words. Never reset between launches: each launch takes a fresh epoch from
+// the claims word on the device (so graph replays do too), and the launch
+// that ends an epoch cycle clears the words itself.
 struct LinearWorkspace {
-  AggWord *words = nullptr;  // tickets and the three status levels (see linear_workspace)
+  AggWord *words = nullptr;  // counters and the three status levels (see linear_workspace)
   int64_t capacity = 0;      // tiles
-  uint32_t epoch = 0;        // epoch of the last launch (0 = never)
 };
+
+static_assert(LinearStatus::kDoneOffset * sizeof(unsigned long long) == 128,
+              "the done count sits 128 bytes into the 256-byte counter header");
+constexpr uint32_t kDefaultEpochCycle = 0xffffffffu;
+uint32_t g_epoch_cycle = kDefaultEpochCycle;
 
 struct S6Workspace {
   void *buf = nullptr;
@@ -69,10 +76,25 @@ int hip_check(hipError_t e, const char *what) {
   return fail(SSM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Returns a workspace holding at least `ntiles` status entries and a fresh
-// epoch for one launch, plus the number of workgroups to launch.
+// A workspace is created or grown only outside HIP graph capture: its
+// allocation, zeroing and the wait for the stream before the old buffer is
+// freed cannot be recorded. Fails when `stream` is capturing.
+static int growth_allowed(hipStream_t stream, const char *what) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();  // not sticky; keep it from reaching the next launch check
+    return SSM_OK;
+  }
+  if (cs == hipStreamCaptureStatusNone) return SSM_OK;
+  return fail(SSM_ERR_INVALID_ARG,
+              std::string(what) + " must be created or grown by a call outside graph capture "
+                                  "(make one call of at least this size on the stream first)");
+}
+
+// Returns a workspace holding at least `ntiles` status entries, plus the
+// number of workgroups to launch.
 static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *status,
-                            uint32_t *epoch, int *grid) {
+                            int *grid) {
   int dev = 0;
   if (int rc = current_device(&dev)) return rc;
   std::lock_guard<std::mutex> lock(g_mu);
@@ -93,11 +115,13 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
   *grid = git->second;
   LinearWorkspace &ws = g_linear[Key(dev, stream)];
   // Layout (each part 256-byte aligned so that the polled status words and
-  // the contended ticket counters never share a cache line):
-  //   [2 tickets][level 0: cap][level 1: cap/64][level 2: cap/4096] entries.
+  // the contended counters never share a cache line):
+  //   [claims word, done count at +128][level 0: cap][level 1: cap/64]
+  //   [level 2: cap/4096] entries.
   auto pad = [](int64_t entries) { return (entries * int64_t(sizeof(AggWord)) + 255) / 256 * 256; };
   auto bytes_for = [&](int64_t cap) { return 256 + pad(cap) + pad(cap / 64) + pad(cap / 4096); };
   if (ws.capacity < ntiles) {
+    if (int rc = growth_allowed(stream, "the linear-scan workspace")) return rc;
     if (ws.words) {
       // The old buffer may still be read by launches queued on this stream.
       if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
@@ -111,7 +135,8 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
     void *p = nullptr;
     if (hipMalloc(&p, bytes) != hipSuccess)
       return fail(SSM_ERR_ALLOC, "hipMalloc of the linear-scan workspace failed");
-    // Zero = epoch 0 everywhere (never written) and both tickets at 0.
+    // Zero = epoch 0 everywhere (never written), and the claims word at
+    // epoch 1 with nothing claimed.
     if (int rc = hip_check(hipMemsetAsync(p, 0, bytes, stream), "hipMemsetAsync")) {
       (void)hipFree(p);
       return rc;
@@ -119,20 +144,13 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
     ws.words = static_cast<AggWord *>(p);
     ws.capacity = cap;
   }
-  if (ws.epoch == 0xffffffffu) {
-    // Epochs are about to wrap: make every old word unambiguous again.
-    if (int rc = hip_check(hipMemsetAsync(ws.words, 0, size_t(bytes_for(ws.capacity)), stream),
-                           "hipMemsetAsync"))
-      return rc;
-    ws.epoch = 0;
-  }
-  ws.epoch += 1;
   char *base = reinterpret_cast<char *>(ws.words);
-  status->ticket = reinterpret_cast<unsigned long long *>(base);
+  status->claims = reinterpret_cast<unsigned long long *>(base);  // done count at +128
   status->lvl0 = reinterpret_cast<AggWord *>(base + 256);
   status->lvl1 = reinterpret_cast<AggWord *>(base + 256 + pad(ws.capacity));
   status->lvl2 = reinterpret_cast<AggWord *>(base + 256 + pad(ws.capacity) + pad(ws.capacity / 64));
-  *epoch = ws.epoch;
+  status->nwords = (bytes_for(ws.capacity) - 256) / int64_t(sizeof(uint64_t));
+  status->epoch_cycle = g_epoch_cycle;
   return SSM_OK;
 }
 
@@ -142,6 +160,7 @@ int s6_workspace(hipStream_t stream, size_t bytes, void **buf) {
   std::lock_guard<std::mutex> lock(g_mu);
   S6Workspace &ws = g_s6[Key(dev, stream)];
   if (ws.bytes < bytes || ws.buf == nullptr) {
+    if (int rc = growth_allowed(stream, "the S6 workspace")) return rc;
     if (ws.buf) {
       // The old buffer may still be read by launches queued on this stream.
       if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
@@ -174,6 +193,7 @@ static int scratch_workspace(hipStream_t stream, size_t bytes, void **buf) {
   std::lock_guard<std::mutex> lock(g_mu);
   ScratchWorkspace &ws = g_scratch[Key(dev, stream)];
   if (ws.bytes < bytes || ws.buf == nullptr) {
+    if (int rc = growth_allowed(stream, "the scratch workspace")) return rc;
     if (ws.buf) {
       if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
       (void)hipFree(ws.buf);
@@ -214,11 +234,10 @@ int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t 
   if (overlap(h, bytes, a, bytes) || overlap(h, bytes, b, bytes))
     return fail(SSM_ERR_INVALID_ARG, "h overlaps a or b");
   LinearStatus status{};
-  uint32_t epoch = 0;
   int grid = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (int rc = linear_workspace(s, ntiles, &status, &epoch, &grid)) return rc;
-  return hip_check(launch_linear_scan(a, b, h0, h, n, ntiles, status, epoch, grid, nullptr,
+  if (int rc = linear_workspace(s, ntiles, &status, &grid)) return rc;
+  return hip_check(launch_linear_scan(a, b, h0, h, n, ntiles, status, grid, nullptr,
                                       nullptr, 0, s),
                    "linear_scan launch");
 }
@@ -243,11 +262,10 @@ int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, flo
   const int64_t tile = linear_tile_elems(true);
   const int64_t ntiles = (n + tile - 1) / tile;
   LinearStatus status{};
-  uint32_t epoch = 0;
   int grid = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (int rc = linear_workspace(s, ntiles, &status, &epoch, &grid)) return rc;
-  return hip_check(launch_linear_scan(a, b, 0.0f, h, n, ntiles, status, epoch, grid, h0, h_last,
+  if (int rc = linear_workspace(s, ntiles, &status, &grid)) return rc;
+  return hip_check(launch_linear_scan(a, b, 0.0f, h, n, ntiles, status, grid, h0, h_last,
                                       uint32_t(len), s),
                    "linear_scan_batched launch");
 }
@@ -389,6 +407,18 @@ const char *ssm_status_string(int code) {
 }
 
 const char *ssm_last_error(void) { return g_last_error.c_str(); }
+
+int ssm_linear_scan_set_epoch_cycle(uint32_t cycle) {
+  g_last_error.clear();
+  if (cycle == 0) return fail(SSM_ERR_INVALID_ARG, "cycle must be >= 1");
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto &kv : g_linear)
+    if (kv.second.words)
+      return fail(SSM_ERR_INVALID_ARG,
+                  "a linear-scan workspace exists; call ssm_release_workspace first");
+  g_epoch_cycle = cycle;
+  return SSM_OK;
+}
 
 int ssm_release_workspace(void) {
   g_last_error.clear();
