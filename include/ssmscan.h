@@ -80,8 +80,9 @@ typedef enum {
  * ordered with each other and with calls on the stream it was recorded on
  * (overlapping launches can corrupt the counters and leave a later launch
  * waiting forever). A call that would create or grow the workspace during
- * capture fails with SSM_ERR_INVALID_ARG; a graph must not outlive its
- * workspace (ssm_release_workspace, or a larger call on that stream, frees it).
+ * capture fails with SSM_ERR_INVALID_ARG. A larger call moves the stream to
+ * a new workspace and keeps the old one, which recorded calls go on using,
+ * until ssm_release_workspace: a graph must not be replayed after that.
  * Errors: SSM_ERR_INVALID_ARG for n < 0, null or non-16-byte-aligned a, b, h
  * with n > 0, or h overlapping a or b; SSM_ERR_ALLOC / SSM_ERR_HIP on
  * runtime failure.
@@ -170,8 +171,9 @@ SSM_API int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *
  * it may be recorded in a HIP graph and replayed (also for the _bf16 and _ex
  * forms); replays and calls on that stream must not overlap (they share the
  * workspace). A call that would create or grow the workspace during capture
- * fails with SSM_ERR_INVALID_ARG; a graph must not outlive its workspace
- * (ssm_release_workspace, or a larger call on that stream, frees it).
+ * fails with SSM_ERR_INVALID_ARG; a grown-out workspace stays allocated for
+ * the calls recorded with it until ssm_release_workspace, after which their
+ * graphs must not be replayed.
  * Errors: SSM_ERR_INVALID_ARG for negative sizes, a bad direction, a
  * null / misaligned pointer with non-zero work, or y overlapping an input;
  * SSM_ERR_UNSUPPORTED for N outside 1..16; zero batch, L or d_inner is a
@@ -234,8 +236,10 @@ SSM_API const char *ssm_status_string(int code);
 /* Detail of the last error raised on the calling thread ("" if none). */
 SSM_API const char *ssm_last_error(void);
 
-/* Frees every cached workspace after synchronising the device(s) that own
- * them. Safe to call at any time from a thread with no call in flight. */
+/* Frees every cached workspace, and those replaced by larger ones, after
+ * synchronising the device(s) that own them. Safe to call at any time from a
+ * thread with no call in flight; graphs recorded before must not be replayed
+ * afterwards. */
 SSM_API int ssm_release_workspace(void);
 
 /*

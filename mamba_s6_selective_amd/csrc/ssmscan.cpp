@@ -9,6 +9,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "../../include/ssmscan.h"
 #include "internal.h"
@@ -56,6 +57,11 @@ struct ScratchWorkspace {
 
 using Key = std::pair<int, hipStream_t>;
 std::mutex g_mu;
+// Buffers replaced by a larger one, per device. A call recorded in a HIP graph
+// keeps the buffer it was recorded with, so a replaced buffer stays allocated
+// until ssm_release_workspace (growth is geometric: at most as much again as
+// the buffers in use).
+std::vector<std::pair<int, void *>> g_retired;
 std::map<Key, LinearWorkspace> g_linear;
 std::map<Key, S6Workspace> g_s6;
 std::map<Key, ScratchWorkspace> g_scratch;
@@ -123,9 +129,7 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
   if (ws.capacity < ntiles) {
     if (int rc = growth_allowed(stream, "the linear-scan workspace")) return rc;
     if (ws.words) {
-      // The old buffer may still be read by launches queued on this stream.
-      if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
-      (void)hipFree(ws.words);
+      g_retired.emplace_back(dev, ws.words);  // queued or recorded launches may still use it
       ws.words = nullptr;
       ws.capacity = 0;
     }
@@ -162,9 +166,7 @@ int s6_workspace(hipStream_t stream, size_t bytes, void **buf) {
   if (ws.bytes < bytes || ws.buf == nullptr) {
     if (int rc = growth_allowed(stream, "the S6 workspace")) return rc;
     if (ws.buf) {
-      // The old buffer may still be read by launches queued on this stream.
-      if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
-      (void)hipFree(ws.buf);
+      g_retired.emplace_back(dev, ws.buf);  // queued or recorded launches may still use it
       ws.buf = nullptr;
       ws.bytes = 0;
     }
@@ -185,8 +187,7 @@ int s6_workspace(hipStream_t stream, size_t bytes, void **buf) {
 }
 
 // Cached scratch buffer for (current device, stream), at least `bytes` long
-// and 256-byte aligned. Growing it waits for the stream, whose queued work
-// may still use the old buffer.
+// and 256-byte aligned.
 static int scratch_workspace(hipStream_t stream, size_t bytes, void **buf) {
   int dev = 0;
   if (int rc = current_device(&dev)) return rc;
@@ -195,8 +196,7 @@ static int scratch_workspace(hipStream_t stream, size_t bytes, void **buf) {
   if (ws.bytes < bytes || ws.buf == nullptr) {
     if (int rc = growth_allowed(stream, "the scratch workspace")) return rc;
     if (ws.buf) {
-      if (int rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize")) return rc;
-      (void)hipFree(ws.buf);
+      g_retired.emplace_back(dev, ws.buf);  // queued or recorded launches may still use it
       ws.buf = nullptr;
       ws.bytes = 0;
     }
@@ -432,6 +432,7 @@ int ssm_release_workspace(void) {
   for (auto &kv : g_linear) devices[kv.first.first] = true;
   for (auto &kv : g_s6) devices[kv.first.first] = true;
   for (auto &kv : g_scratch) devices[kv.first.first] = true;
+  for (auto &r : g_retired) devices[r.first] = true;
   for (auto &dv : devices) {
     if (hipSetDevice(dv.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
       rc = fail(SSM_ERR_HIP, "hipDeviceSynchronize failed while releasing workspaces");
@@ -451,9 +452,14 @@ int ssm_release_workspace(void) {
     (void)hipSetDevice(kv.first.first);
     (void)hipFree(kv.second.buf);
   }
+  for (auto &r : g_retired) {
+    (void)hipSetDevice(r.first);
+    (void)hipFree(r.second);
+  }
   g_linear.clear();
   g_s6.clear();
   g_scratch.clear();
+  g_retired.clear();
   (void)hipSetDevice(saved);
   return rc;
 }

@@ -171,3 +171,48 @@ def test_workspace_growth_during_capture_is_refused():
     ref = ssm.linear_scan(a, b, 0.0)
     torch.cuda.synchronize()
     assert torch.equal(_bits(y), _bits(ref))
+
+
+def test_graph_replay_after_workspace_growth():
+    """A larger call on the capture stream moves the stream to a larger
+    workspace; the recorded calls keep the workspaces they were recorded
+    with, which stay allocated until release_workspace."""
+    dev = need_gpu()
+    say("graph replay after workspace growth")
+    a, b = (t.to(dev) for t in linear_inputs(3 * TILE + 17, seed=81, a_lo=0.5, a_hi=1.0))
+    big = 4100 * TILE + 5  # past the smallest linear workspace (4096 tiles)
+    a2, b2 = (t.to(dev) for t in linear_inputs(big, seed=82, a_lo=0.5, a_hi=1.0))
+    small = s6_inputs(1, 512, 128, 16, seed=83, dtype="f32")
+    large = s6_inputs(2, 4096, 512, 16, seed=84, dtype="f32")  # a larger S6 workspace
+    ts = [x.to(dev) for x in (small.u, small.delta, small.A, small.B, small.C, small.D)]
+    tl = [x.to(dev) for x in (large.u, large.delta, large.A, large.B, large.C, large.D)]
+    ref_lin, ref_lin2 = ssm.linear_scan(a, b, 0.5), ssm.linear_scan(a2, b2, -0.5)
+    ref_s6, ref_s6l = ssm.selective_scan_fwd(*ts), ssm.selective_scan_fwd(*tl)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    y = torch.empty_like(ref_lin)
+    ys6 = torch.empty_like(ref_s6)
+    with torch.cuda.stream(s):  # size the stream's workspaces for the small calls
+        ssm.linear_scan(a, b, 0.5, out=y)
+        ssm.selective_scan_fwd(*ts, out=ys6)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ssm.linear_scan(a, b, 0.5, out=y)
+        ssm.selective_scan_fwd(*ts, out=ys6)
+    torch.cuda.synchronize()
+    for k in range(3):
+        with torch.cuda.stream(s):  # larger calls: new workspaces for s (grown on the first)
+            h2 = ssm.linear_scan(a2, b2, -0.5)
+            yl = ssm.selective_scan_fwd(*tl)
+        s.synchronize()
+        assert torch.equal(_bits(h2), _bits(ref_lin2)), k
+        assert torch.equal(_bits(yl), _bits(ref_s6l)), k
+        y.fill_(float("nan"))
+        ys6.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        assert torch.equal(_bits(y), _bits(ref_lin)), k
+        assert torch.equal(_bits(ys6), _bits(ref_s6)), k
