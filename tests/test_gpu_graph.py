@@ -142,6 +142,29 @@ def test_linear_epoch_cycle_clears_status_words():
             torch.cuda.synchronize()
             for i, (k, h) in enumerate(outs):
                 assert torch.equal(_bits(h), _bits(refs[k])), (cycle, i, k)
+            if cycle == 2:
+                # Replays that end cycles themselves: a recorded large call
+                # and eager small calls alternate on one workspace.
+                st = torch.cuda.Stream()
+                y = torch.empty_like(refs["big"])
+                with torch.cuda.stream(st):
+                    ssm.linear_scan(a_big, b_big, 1.5, out=y)
+                st.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=st):
+                    ssm.linear_scan(a_big, b_big, 1.5, out=y)
+                torch.cuda.synchronize()
+                for r in range(5):
+                    y.fill_(float("nan"))
+                    torch.cuda.synchronize()
+                    with torch.cuda.stream(st):
+                        g.replay()
+                        hs = ssm.linear_scan(a_sm, b_sm, 0.0) if r % 2 else None
+                    st.synchronize()
+                    assert torch.equal(_bits(y), _bits(refs["big"])), ("replay", r)
+                    if hs is not None:
+                        assert torch.equal(_bits(hs), _bits(refs["small"])), ("replay", r)
+                del g
     finally:
         ssm.release_workspace()
         ssm.linear_scan_set_epoch_cycle(2**32 - 1)
