@@ -395,3 +395,21 @@ def test_s6_fused_softplus_full_size():
     d_eff = oracle.softplus(inp.delta_pre.double().numpy())
     ref = native.selective_scan(inp.u, d_eff, inp.A, inp.B, inp.C, inp.D, "fwd")[0]
     assert_close(y, ref, TOL["bf16"], name)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", list(range(1, 17)))
+def test_s6_every_state_count(N, dt):
+    """Every state count N compiles its own kernels (per input type and delta
+    mode): each is checked, bidirectionally so that both sweeps, the carry
+    and both fixes run, on a shape with several chunks, a ragged last block
+    and ragged channels; and with softplus(delta + bias) fused in."""
+    say(f"s6 N={N} {dt}")
+    inp = s6_inputs(2, 700, 72, N, seed=500 + N, dtype=dt)
+    assert_close(gpu_s6(inp, "bidir"), ref_s6(inp, "bidir", use_c=True), TOL[dt], f"N={N}")
+    raw = (inp.delta_pre.float() * 6.0).to(inp.delta_pre.dtype)
+    bias = torch.randn(72, generator=torch.Generator().manual_seed(N)) * 2.0
+    ref = oracle.selective_scan(inp.u.double().numpy(), raw.double().numpy(), inp.A.numpy(),
+                                inp.B.double().numpy(), inp.C.double().numpy(), inp.D.numpy(),
+                                "bidir", delta_bias=bias.numpy(), delta_softplus=True)
+    assert_close(gpu_s6_fused(inp, raw, bias, "bidir"), ref, TOL[dt], f"N={N} fused")
