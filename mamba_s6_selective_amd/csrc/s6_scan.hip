@@ -443,16 +443,35 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
   const int d = dg * 64 + lane;
   const bool valid = d < g.d_inner;
   const bool fwd = direction != SSM_DIR_REV, rev = direction != SSM_DIR_FWD;
-  const float Ap = valid ? A[size_t(d) * NT + n] * kLog2e : 0.0f;
   const int k0 = part * kCarryPart;
-  float ra[kCarryPart], rf[kCarryPart], rr[kCarryPart];
+  // All loads first, from indices clamped into range (lanes past d_inner and
+  // chunks past the end read valid entries whose values are then replaced),
+  // so that they are in flight together: a load under a per-lane condition
+  // whose value feeds an exp in the same branch would be waited for one at a
+  // time.
+  const int dc = valid ? d : 0;
+  const float Aval = A[size_t(dc) * NT + n];
+  float ra[kCarryPart], rf[kCarryPart] = {}, rr[kCarryPart] = {};
+#pragma unroll
+  for (int i = 0; i < kCarryPart; ++i)
+    ra[i] = agg_s[sum_index(g, b, min(k0 + i, g.nchunks - 1), dc)];
+  if (fwd) {
+#pragma unroll
+    for (int i = 0; i < kCarryPart; ++i)
+      rf[i] = agg_f[agg_index(g, NT, b, min(k0 + i, g.nchunks - 1), n, dc)];
+  }
+  if (rev) {
+#pragma unroll
+    for (int i = 0; i < kCarryPart; ++i)
+      rr[i] = agg_r[agg_index(g, NT, b, min(k0 + i, g.nchunks - 1), n, dc)];
+  }
+  const float Ap = valid ? Aval * kLog2e : 0.0f;
 #pragma unroll
   for (int i = 0; i < kCarryPart; ++i) {
-    const int k = k0 + i;
-    const bool in = valid && k < g.nchunks;  // chunks past the end act as identity maps
-    ra[i] = in ? exp2_hw(Ap * agg_s[sum_index(g, b, k, d)]) : 1.0f;
-    rf[i] = in && fwd ? agg_f[agg_index(g, NT, b, k, n, d)] : 0.0f;
-    rr[i] = in && rev ? agg_r[agg_index(g, NT, b, k, n, d)] : 0.0f;
+    const bool in = valid && k0 + i < g.nchunks;  // chunks past the end act as identity maps
+    ra[i] = in ? exp2_hw(Ap * ra[i]) : 1.0f;
+    rf[i] = in && fwd ? rf[i] : 0.0f;
+    rr[i] = in && rev ? rr[i] : 0.0f;
   }
   float ta = 1.0f, tf = 0.0f, tr = 0.0f;
 #pragma unroll
