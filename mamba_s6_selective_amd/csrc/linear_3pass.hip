@@ -247,7 +247,8 @@ __global__ __launch_bounds__(kThreads) void local_hs_kernel(const float *__restr
 // totals are scanned (wave DPP scans, then the waves' totals in LDS), and each
 // thread re-walks its tiles writing the value of h entering each. A thread's
 // aggregates are read kBatch at a time into registers, so that their loads
-// are in flight together and the re-walk reads no memory.
+// are in flight together (and, up to kBatch tiles per thread, the re-walk
+// reads no memory).
 constexpr int kCarryThreads = 1024;
 constexpr int kBatch = 16;
 
@@ -261,15 +262,28 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(const float *__res
   const int64_t t0 = int64_t(threadIdx.x) * per;
   const bool cached = per <= kBatch;  // same for every thread
   float ra[kBatch], rb[kBatch];
-  float ta = 1.0f, tb = 0.0f;
-  for (int64_t k0 = 0; k0 < per; k0 += kBatch) {
+  // Reads the thread's aggregates k0 .. k0 + kBatch - 1; entries past its
+  // range or past the end become the identity. Every load is issued from an
+  // index clamped into range before any is used (a load under a per-lane
+  // condition would be waited for on its own).
+  auto load_batch = [&](int64_t k0) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int64_t t = t0 + k0 + j;
-      const bool in = k0 + j < per && t < ntiles;  // past the end: the identity
-      ra[j] = in ? agg[2 * t] : 1.0f;
-      rb[j] = in ? agg[2 * t + 1] : 0.0f;
+      const int64_t tc = t < ntiles ? t : ntiles - 1;
+      ra[j] = agg[2 * tc];
+      rb[j] = agg[2 * tc + 1];
     }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool in = k0 + j < per && t0 + k0 + j < ntiles;
+      ra[j] = in ? ra[j] : 1.0f;
+      rb[j] = in ? rb[j] : 0.0f;
+    }
+  };
+  float ta = 1.0f, tb = 0.0f;
+  for (int64_t k0 = 0; k0 < per; k0 += kBatch) {
+    load_batch(k0);
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) compose(ta, tb, ra[j], rb[j], ta, tb);
   }
@@ -295,11 +309,13 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(const float *__res
       h = __builtin_fmaf(ra[j], h, rb[j]);
     }
   } else {
-    for (int64_t k = 0; k < per; ++k) {
-      const int64_t t = t0 + k;
-      if (t < ntiles) {
-        hin[t] = h;
-        h = __builtin_fmaf(agg[2 * t], h, agg[2 * t + 1]);
+    for (int64_t k0 = 0; k0 < per; k0 += kBatch) {
+      load_batch(k0);
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t t = t0 + k0 + j;
+        if (k0 + j < per && t < ntiles) hin[t] = h;
+        h = __builtin_fmaf(ra[j], h, rb[j]);
       }
     }
   }
