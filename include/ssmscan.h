@@ -124,7 +124,9 @@ SSM_API int ssm_linear_scan_batched(const float *a, const float *b, const float 
  * aggregates, an apply pass writes h = A * h_in + B. 28 bytes of HBM traffic
  * per element instead of 12. Deterministic; not bitwise equal to
  * ssm_linear_scan (different association). Uses a library-owned scratch
- * workspace of about 8 bytes per element, cached per (device, stream).
+ * workspace of about 8 bytes per element, cached per (device, stream); one
+ * replaced by a larger call stays allocated until ssm_release_workspace, so
+ * growth can hold up to twice the largest size.
  * Errors: as ssm_linear_scan, and SSM_ERR_UNSUPPORTED for n > 2^31.
  */
 SSM_API int ssm_linear_scan_3pass(const float *a, const float *b, float h0, float *h, int64_t n,

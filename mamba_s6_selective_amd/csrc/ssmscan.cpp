@@ -83,8 +83,7 @@ int hip_check(hipError_t e, const char *what) {
 }
 
 // A workspace is created or grown only outside HIP graph capture: its
-// allocation, zeroing and the wait for the stream before the old buffer is
-// freed cannot be recorded. Fails when `stream` is capturing.
+// allocation and zeroing cannot be recorded. Fails when `stream` is capturing.
 static int growth_allowed(hipStream_t stream, const char *what) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
