@@ -243,80 +243,71 @@ __global__ __launch_bounds__(kThreads) void local_hs_kernel(const float *__restr
   }
 }
 
-// One workgroup: thread i folds tiles [i*per, (i+1)*per), the threads'
-// totals are scanned (wave DPP scans, then the waves' totals in LDS), and each
-// thread re-walks its tiles writing the value of h entering each. A thread's
-// aggregates are read kBatch at a time into registers, so that their loads
-// are in flight together (and, up to kBatch tiles per thread, the re-walk
-// reads no memory).
+// One workgroup of kCarryWaves waves. Wave w owns rows [w*rows, (w+1)*rows)
+// of 64 consecutive tile aggregates, lane l holding tile row*64 + l, so every
+// load of a row and every store of its incoming values moves 64 neighbouring
+// entries. First walk: each row is scanned across lanes (DPP) and the rows'
+// totals are composed in order into the wave's total; the totals meet in LDS.
+// Second walk: each wave goes over its rows again from the composition of the
+// waves before it, writing the value of h entering each tile. Rows are read
+// kBatch at a time, every load issued before any is used (and, up to kBatch
+// rows per wave, the second walk reads no memory). Fixed shapes, so the
+// result is deterministic.
 constexpr int kCarryThreads = 1024;
+constexpr int kCarryWaves = kCarryThreads / 64;
 constexpr int kBatch = 16;
 
 __global__ __launch_bounds__(kCarryThreads) void carry_kernel(const float *__restrict__ agg,
                                                               float *__restrict__ hin,
                                                               float h0, int64_t ntiles,
-                                                              int64_t per) {
-  __shared__ float s_a[kCarryThreads / 64], s_b[kCarryThreads / 64];
+                                                              int64_t rows) {
+  __shared__ float s_a[kCarryWaves], s_b[kCarryWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t t0 = int64_t(threadIdx.x) * per;
-  const bool cached = per <= kBatch;  // same for every thread
-  float ra[kBatch], rb[kBatch];
-  // Reads the thread's aggregates k0 .. k0 + kBatch - 1; entries past its
-  // range or past the end become the identity. Every load is issued from an
-  // index clamped into range before any is used (a load under a per-lane
-  // condition would be waited for on its own).
-  auto load_batch = [&](int64_t k0) {
+  const int64_t first = int64_t(wave) * rows;  // the wave's first row
+  float ia[kBatch], ib[kBatch];                // inclusive scans of a batch of rows
+  // Rows k0 .. k0 + kBatch - 1 of the wave, each scanned across lanes; tiles
+  // past the wave's rows or past the end are the identity.
+  auto scan_batch = [&](int64_t k0) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int64_t t = t0 + k0 + j;
+      const int64_t t = (first + k0 + j) * 64 + lane;
       const int64_t tc = t < ntiles ? t : ntiles - 1;
-      ra[j] = agg[2 * tc];
-      rb[j] = agg[2 * tc + 1];
+      ia[j] = agg[2 * tc];
+      ib[j] = agg[2 * tc + 1];
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const bool in = k0 + j < per && t0 + k0 + j < ntiles;
-      ra[j] = in ? ra[j] : 1.0f;
-      rb[j] = in ? rb[j] : 0.0f;
+      const bool in = k0 + j < rows && (first + k0 + j) * 64 + lane < ntiles;
+      ia[j] = in ? ia[j] : 1.0f;
+      ib[j] = in ? ib[j] : 0.0f;
+      wave_scan(ia[j], ib[j]);
     }
   };
-  float ta = 1.0f, tb = 0.0f;
-  for (int64_t k0 = 0; k0 < per; k0 += kBatch) {
-    load_batch(k0);
+  float ta = 1.0f, tb = 0.0f;  // the wave's total, the same in every lane
+  for (int64_t k0 = 0; k0 < rows; k0 += kBatch) {
+    scan_batch(k0);
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) compose(ta, tb, ra[j], rb[j], ta, tb);
+    for (int j = 0; j < kBatch; ++j) compose(ta, tb, lane_f(ia[j], 63), lane_f(ib[j], 63), ta, tb);
   }
-  float ia = ta, ib = tb;
-  wave_scan(ia, ib);
-  if (lane == 63) {
-    s_a[wave] = ia;
-    s_b[wave] = ib;
+  if (lane == 0) {
+    s_a[wave] = ta;
+    s_b[wave] = tb;
   }
   __syncthreads();
   float wa = 1.0f, wb = 0.0f;  // earlier waves
   for (int w = 0; w < wave; ++w) compose(wa, wb, s_a[w], s_b[w], wa, wb);
-  const float xa = dpp<kWaveShr1, 0xf, 0xf>(1.0f, ia);  // earlier lanes of this wave
-  const float xb = dpp<kWaveShr1, 0xf, 0xf>(0.0f, ib);
-  float pa, pb;
-  compose(wa, wb, xa, xb, pa, pb);
-  float h = __builtin_fmaf(pa, h0, pb);
-  if (cached) {
+  float h = __builtin_fmaf(wa, h0, wb);  // entering the wave's first row
+  const bool cached = rows <= kBatch;    // same for every wave
+  for (int64_t k0 = 0; k0 < rows; k0 += kBatch) {
+    if (!cached) scan_batch(k0);
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int64_t t = t0 + j;
-      if (j < per && t < ntiles) hin[t] = h;
-      h = __builtin_fmaf(ra[j], h, rb[j]);
-    }
-  } else {
-    for (int64_t k0 = 0; k0 < per; k0 += kBatch) {
-      load_batch(k0);
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int64_t t = t0 + k0 + j;
-        if (k0 + j < per && t < ntiles) hin[t] = h;
-        h = __builtin_fmaf(ra[j], h, rb[j]);
-      }
+      const float xa = dpp<kWaveShr1, 0xf, 0xf>(1.0f, ia[j]);  // earlier lanes of the row
+      const float xb = dpp<kWaveShr1, 0xf, 0xf>(0.0f, ib[j]);
+      const int64_t t = (first + k0 + j) * 64 + lane;
+      if (k0 + j < rows && t < ntiles) hin[t] = __builtin_fmaf(xa, h, xb);
+      h = __builtin_fmaf(lane_f(ia[j], 63), h, lane_f(ib[j], 63));
     }
   }
 }
@@ -369,9 +360,9 @@ hipError_t launch_linear_scan_3pass(const float *a, const float *b, float h0, fl
     hipLaunchKernelGGL(local_kernel, dim3(unsigned(ntiles)), dim3(kThreads), 0, stream, a, b, pa,
                        pb, agg, n);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  const int64_t per = (ntiles + kCarryThreads - 1) / kCarryThreads;
+  const int64_t rows = (ntiles + kCarryThreads - 1) / kCarryThreads;  // per wave, of 64 tiles
   hipLaunchKernelGGL(carry_kernel, dim3(1), dim3(kCarryThreads), 0, stream, agg, hin, h0, ntiles,
-                     per);
+                     rows);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const int64_t groups = (n + 1023) / 1024;
   hipLaunchKernelGGL(apply_kernel, dim3(unsigned(groups)), dim3(256), 0, stream, pa, pb, hin, h,
