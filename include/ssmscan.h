@@ -23,6 +23,12 @@
  *                                  settings give bit-identical outputs.
  *   SSMSCAN_LINEAR_WGS_PER_CU=<k>  caps the workgroups per CU of the single-
  *                                  pass linear scan (read once per device).
+ *   SSMSCAN_LINEAR_EPOCH_CYCLE=<c> epochs per cycle of the single-pass scans'
+ *                                  status words (1 .. 2^31 - 1, the default),
+ *                                  read when a stream's workspace is created;
+ *                                  a short cycle exercises the launch that
+ *                                  clears the words. Results do not depend
+ *                                  on it.
  */
 #ifndef SSMSCAN_H
 #define SSMSCAN_H
@@ -70,6 +76,12 @@ typedef enum {
  * bitwise identical from run to run (the cross-tile carry is always folded in
  * the same left-to-right order). It is not bitwise equal to a sequential fp32
  * loop: partial products are associated differently.
+ * Non-finite inputs (and h0) give the values the sequential loop gives, inf
+ * and NaN in the same places: a product of multipliers that underflows in
+ * fp32 is kept as the smallest subnormal of its sign, never 0, so an infinite
+ * state pushed through it stays infinite, while an exactly-zero multiplier
+ * acts as in the loop (0 times an infinite state is NaN). Products of
+ * multipliers above 1 that overflow are outside this guarantee.
  * Uses a library-owned workspace cached per (device, stream): counters and
  * epoch-tagged status words that every launch leaves ready for the next, the
  * epoch advancing on the device. So once a call on `stream` has sized that
@@ -103,10 +115,10 @@ SSM_API int ssm_linear_scan(const float *a, const float *b, float h0, float *h, 
  * h0     : const float[nseq] or NULL (all sequences start from 0).
  * h_last : float[nseq] or NULL; receives h[k][len-1].
  * One single-pass launch whatever the shape (the sequences are segments of one
- * look-back scan). Deterministic. Within this call a multiplier of exactly
- * zero discards the state before it even when that state is inf or NaN (IEEE
- * arithmetic, and ssm_linear_scan, would give NaN); this is what keeps one
- * sequence's non-finite values out of the next.
+ * look-back scan). Deterministic. Every sequence starts from its own h0
+ * whatever the previous one ended with (inf and NaN included): sequence
+ * starts are marked explicitly, not inferred from zero multipliers. Inside a
+ * sequence values, non-finite ones included, are as ssm_linear_scan gives.
  * Errors: SSM_ERR_INVALID_ARG for negative sizes, a null / misaligned a, b,
  * h with work to do, or h / h_last overlapping an input or each other;
  * SSM_ERR_UNSUPPORTED for nseq * len > 2^31; nseq == 0 or len == 0 is a
@@ -243,18 +255,6 @@ SSM_API const char *ssm_last_error(void);
  * thread with no call in flight; graphs recorded before must not be replayed
  * afterwards. */
 SSM_API int ssm_release_workspace(void);
-
-/*
- * Diagnostic. The single-pass scans tag their status words with a 32-bit
- * epoch taken from the device; after `cycle` launches on one workspace (by
- * default 2^32 - 1, all non-zero tags) the epochs start again at 1, and the
- * launch that ends a cycle clears every status word first. This sets the
- * cycle for workspaces created afterwards, so that the clearing can be
- * exercised with few calls; results do not depend on it.
- * Errors: SSM_ERR_INVALID_ARG for cycle == 0 or while a linear-scan workspace
- * exists (call ssm_release_workspace first).
- */
-SSM_API int ssm_linear_scan_set_epoch_cycle(uint32_t cycle);
 
 #ifdef __cplusplus
 }

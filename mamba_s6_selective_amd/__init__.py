@@ -38,7 +38,6 @@ SIGNATURES = {
     "ssm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ssm_last_error": (ctypes.c_char_p, []),
     "ssm_release_workspace": (ctypes.c_int, []),
-    "ssm_linear_scan_set_epoch_cycle": (ctypes.c_int, [ctypes.c_uint32]),
 }
 
 _lib = None
@@ -269,11 +268,3 @@ def copy_f32(src, dst):
 
 def release_workspace():
     _check(load_library().ssm_release_workspace())
-
-
-def linear_scan_set_epoch_cycle(cycle: int):
-    """Epoch cycle of the single-pass scans' status words for workspaces made
-    afterwards (diagnostic; default 2**32 - 1; needs release_workspace first)."""
-    if not 1 <= int(cycle) < 2**32:
-        raise ValueError("cycle must be in [1, 2**32)")
-    _check(load_library().ssm_linear_scan_set_epoch_cycle(int(cycle)))

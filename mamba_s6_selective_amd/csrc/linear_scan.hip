@@ -78,34 +78,72 @@ struct Shape {
 
 using namespace scan;
 
+// Status words: bits 63..32 hold the launch's epoch (bit 63 of the multiplier
+// word: the aggregate holds a sequence head, batched scans only), bits 31..0
+// the fp32 payload. Epochs stay below 2^31.
+constexpr uint64_t kHeadBit = uint64_t(1) << 63;
+
 __device__ __forceinline__ uint64_t ld_status(const uint64_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_status(uint64_t *p, uint32_t epoch, float v) {
-  const uint64_t w = (uint64_t(epoch) << 32) | uint64_t(__float_as_uint(v));
+__device__ __forceinline__ void st_status(uint64_t *p, uint32_t epoch, float v,
+                                          uint32_t head = 0u) {
+  const uint64_t w = (uint64_t(epoch) << 32) | uint64_t(__float_as_uint(v)) |
+                     (head ? kHeadBit : uint64_t(0));
   __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float payload(uint64_t w) {
-  return __uint_as_float(uint32_t(w));
+__device__ __forceinline__ void st_map(AggWord &w, uint32_t epoch, const Map &m) {
+  st_status(&w.a, epoch, m.a, m.head);
+  st_status(&w.b, epoch, m.b);
+}
+__device__ __forceinline__ Map word_map(uint64_t wa, uint64_t wb) {
+  return Map{__uint_as_float(uint32_t(wa)), __uint_as_float(uint32_t(wb)),
+             (wa & kHeadBit) ? 1u : 0u};
 }
 
 __device__ __forceinline__ bool word_ready(uint64_t w, uint32_t epoch) {
-  return uint32_t(w >> 32) == epoch;
+  return (uint32_t(w >> 32) & 0x7fffffffu) == epoch;
 }
 
-// Composition, in lane order, of the pairs held by lanes [0, count) of the
+// Composition, in lane order, of the maps held by lanes [0, count) of the
 // wave (later lanes contribute the identity). Fixed DPP tree: the result
-// depends only on the values and `count`. Returned in every lane.
+// depends only on the values and `count`. Returned in every lane. Op is a
+// careful rule; when every word of the window is finite and no head, the
+// plain rule gives the same values except that a total multiplier that
+// underflowed must be nudged (unless a word's multiplier is exactly zero),
+// which is what the common case does.
+// The careful case is rare; it runs as a loop of cross-lane shuffles (one
+// copy of the code, not one per window: unrolled DPP steps at every window
+// doubled the control wave's code and slowed the scan through instruction
+// fetch). Still a fixed shape, so the result depends only on the words.
 template <class Op>
-__device__ __forceinline__ void window_total(float a, float b, int count, int lane, float &ta,
-                                             float &tb) {
-  if (lane >= count) {
-    a = 1.0f;
-    b = 0.0f;
+__device__ __forceinline__ Map window_total_careful(Map m) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll 1
+  for (int d = 1; d < 64; d *= 2) {
+    Map p;
+    p.a = __shfl_up(m.a, d);
+    p.b = __shfl_up(m.b, d);
+    p.head = uint32_t(__shfl_up(int(m.head), d));
+    if (lane >= d) m = Op::compose(p, m);
   }
-  wave_scan<Op>(a, b);
-  ta = lane_f(a, 63);
-  tb = lane_f(b, 63);
+  return lane_map(m, 63);
+}
+// Seg: heads are common (the batched form), so the plain rule honours them;
+// otherwise a head (a tile evaluated in sequence) is rare and takes the
+// careful path with the non-finite words.
+template <class Op, bool Seg>
+__device__ __forceinline__ Map window_total(Map m, int count, int lane) {
+  if (lane >= count) m = identity_map();
+  const bool odd =
+      !__builtin_isfinite(m.a) || !__builtin_isfinite(m.b) || (!Seg && m.head != 0u);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(odd) != 0, 0))  // uniform; rare
+    return window_total_careful<Op>(m);
+  const bool zero = __builtin_amdgcn_ballot_w64(m.a == 0.0f) != 0;
+  wave_scan<AffOp<Seg, false>>(m);
+  Map t = lane_map(m, 63);
+  if (t.a == 0.0f && !zero) t.a = nudge(t.a);
+  return t;
 }
 
 // Look-back windows at level 0: the tile's own superblock and the
@@ -131,7 +169,8 @@ struct LookBack {
 // everything from the start of block blk1 up to its superblock, and h_in
 // (h0 pushed through the level-2 prefix, then PB, then P0).
 struct Prefix {
-  float p0a, p0b, pba, pbb, h_in;
+  Map p0, pb;
+  float h_in;
 };
 
 __device__ __forceinline__ void lb_init(LookBack &s, int64_t tile, int lane) {
@@ -192,52 +231,43 @@ __device__ __forceinline__ bool lb_done(const LookBack &s) {
 }
 
 // Composition of the complete look-back windows (fixed shapes: the result
-// depends only on the words and the tile index).
-template <class Op>
+// depends only on the words and the tile index). Op is a careful rule: the
+// published aggregates' multipliers are usually underflowed products.
+template <class Op, bool Seg>
 __device__ Prefix lb_finish(const LookBack &s, float h0, int lane) {
-  float p2a, p2b, pba, pbb;
-  window_total<Op>(payload(s.w2a), payload(s.w2b), s.n2, lane, p2a, p2b);
-  window_total<Op>(payload(s.w1a), payload(s.w1b), s.n1, lane, pba, pbb);
+  const Map p2 = window_total<Op, Seg>(word_map(s.w2a, s.w2b), s.n2, lane);
+  Map pb = window_total<Op, Seg>(word_map(s.w1a, s.w1b), s.n1, lane);
   Prefix pf;
+  pf.p0 = identity_map();
 #pragma unroll
   for (int q = 0; q < kRecent; ++q) {
     if (q < s.nw - 1) {  // a whole earlier superblock
-      float qa, qb;
-      window_total<Op>(payload(s.wa[q]), payload(s.wb[q]), kFan, lane, qa, qb);
-      Op::compose(pba, pbb, qa, qb, pba, pbb);
+      pb = Op::compose(pb, window_total<Op, Seg>(word_map(s.wa[q], s.wb[q]), kFan, lane));
     } else if (q == s.nw - 1) {  // the tile's own superblock, up to the tile
-      window_total<Op>(payload(s.wa[q]), payload(s.wb[q]), s.n0, lane, pf.p0a, pf.p0b);
+      pf.p0 = window_total<Op, Seg>(word_map(s.wa[q], s.wb[q]), s.n0, lane);
     }
   }
-  pf.pba = pba;
-  pf.pbb = pbb;
-  const float h2 = Op::apply(p2a, h0, p2b);
-  const float h1 = Op::apply(pba, h2, pbb);
-  pf.h_in = Op::apply(pf.p0a, h1, pf.p0b);
+  pf.pb = pb;
+  const float h2 = Op::apply(p2, h0);
+  const float h1 = Op::apply(pb, h2);
+  pf.h_in = Op::apply(pf.p0, h1);
   return pf;
 }
 
-// Once a tile's own aggregate (ga, gb) is known: the last tile of a
-// superblock publishes the superblock's aggregate (level 1), and the last tile
-// of a block the block's aggregate (level 2). For the last tile of a block,
-// blk1 is its own block, so PB (+) P0 (+) own covers the whole block.
+// Once a tile's own aggregate is known: the last tile of a superblock
+// publishes the superblock's aggregate (level 1), and the last tile of a
+// block the block's aggregate (level 2). For the last tile of a block, blk1
+// is its own block, so PB (+) P0 (+) own covers the whole block.
 template <class Op>
 __device__ __forceinline__ void publish_higher(const LinearStatus &st, int64_t tile,
-                                               const Prefix &pf, float ga, float gb,
-                                               uint32_t epoch, int lane) {
+                                               const Prefix &pf, const Map &own, uint32_t epoch,
+                                               int lane) {
   const int64_t sb = tile / kFan;
   const int64_t blk = sb / kFan;
   if (tile - sb * kFan != kFan - 1 || lane != 0) return;
-  float sba, sbb;
-  Op::compose(pf.p0a, pf.p0b, ga, gb, sba, sbb);  // P0 (+) own aggregate
-  st_status(&st.lvl1[sb].a, epoch, sba);
-  st_status(&st.lvl1[sb].b, epoch, sbb);
-  if (sb - blk * kFan == kFan - 1) {
-    float ba, bb;
-    Op::compose(pf.pba, pf.pbb, sba, sbb, ba, bb);
-    st_status(&st.lvl2[blk].a, epoch, ba);
-    st_status(&st.lvl2[blk].b, epoch, bb);
-  }
+  const Map sbm = Op::compose(pf.p0, own);
+  st_map(st.lvl1[sb], epoch, sbm);
+  if (sb - blk * kFan == kFan - 1) st_map(st.lvl2[blk], epoch, Op::compose(pf.pb, sbm));
 }
 
 // Independent sequences inside one scan (the batched form): `len` elements
@@ -270,14 +300,31 @@ __device__ __forceinline__ bool seg_edge(uint32_t i, const Segments &sg) {
   return t == 0 || t + 4 >= sg.len;
 }
 
+// Bit j set when element i + j (j < 4, below n) is the first of a sequence.
+__device__ __forceinline__ uint32_t seg_heads(int64_t i, int64_t n, const Segments &sg) {
+  uint32_t bits = 0;
+  if (i < n && seg_edge(uint32_t(i), sg)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (i + j < n) {
+        uint32_t k, t;
+        seg_pos(uint32_t(i + j), sg, k, t);
+        if (t == 0) bits |= 1u << j;
+      }
+    }
+  }
+  return bits;
+}
+
 // Loads one tile (rows of float4 per wave); past n the identity map (1, 0).
-// With segments, the first element of every sequence becomes the constant
-// map (0, a*h0 + b): it ignores whatever precedes it.
+// With segments, the first element of every sequence has its b replaced by
+// a*h0 + b (its value, whatever precedes it) and its head bit set in hd.
 template <bool Seg>
 __device__ __forceinline__ void load_tile(const float *__restrict__ a,
                                           const float *__restrict__ b, int64_t n, int64_t tile,
                                           const Segments &sg, float4 (&va)[Shape<Seg>::kRows],
-                                          float4 (&vb)[Shape<Seg>::kRows]) {
+                                          float4 (&vb)[Shape<Seg>::kRows],
+                                          uint32_t (&hd)[Shape<Seg>::kRows]) {
   constexpr int kRows = Shape<Seg>::kRows, kWaveElems = Shape<Seg>::kWaveElems,
                 kTileElems = Shape<Seg>::kTileElems;
   const int lane = threadIdx.x & 63;
@@ -305,22 +352,23 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ a,
       vb[r] = make_float4(tb[0], tb[1], tb[2], tb[3]);
     }
   }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) hd[r] = 0u;
   if constexpr (Seg) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const int64_t off = wave_start + r * kRowElems + lane * 4;
-      if (off < n && seg_edge(uint32_t(off), sg)) {
+      hd[r] = seg_heads(off, n, sg);
+      if (hd[r]) {
         float ta[4] = {va[r].x, va[r].y, va[r].z, va[r].w};
         float tb[4] = {vb[r].x, vb[r].y, vb[r].z, vb[r].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (off + j < n) {
+          if ((hd[r] >> j) & 1u) {
             uint32_t k, t;
             seg_pos(uint32_t(off + j), sg, k, t);
-            if (t == 0) {
-              tb[j] = __builtin_fmaf(ta[j], sg.h0 ? sg.h0[k] : 0.0f, tb[j]);
-              ta[j] = 0.0f;
-            }
+            tb[j] = __builtin_fmaf(ta[j], sg.h0 ? sg.h0[k] : 0.0f, tb[j]);
+            ta[j] = 0.0f;
           }
         }
         va[r] = make_float4(ta[0], ta[1], ta[2], ta[3]);
@@ -330,45 +378,73 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ a,
   }
 }
 
-// Data waves, phase 1: chunk aggregates of the lane's 4 items per row, a wave
-// scan per row, and the wave's aggregate (rows folded in order) into LDS.
-template <class Op, int kRows>
-__device__ __forceinline__ void tile_local_scan(const float4 (&va)[kRows],
-                                                const float4 (&vb)[kRows], float (&ia)[kRows],
-                                                float (&ib)[kRows], float *s_wave_a,
-                                                float *s_wave_b) {
+__device__ __forceinline__ Map item_map(float a, float b, uint32_t hd, int j) {
+  return Map{a, b, (hd >> j) & 1u};
+}
+
+// Data waves, phase 1: the lane's 4 items composed, a wave scan per row (im:
+// the lane's inclusive prefix within its row) and the wave's aggregate (rows
+// folded in order), returned in every lane. Plain products; a multiplier
+// that underflowed to zero is nudged where it is used later (im and the row
+// totals) unless the lanes it covers hold an exact zero multiplier, so the
+// results stay right when an infinite carry arrives later. Returns true if
+// the wave holds an inf or NaN (then a plain product may have formed 0 * inf
+// and an offset may have met an underflowed zero, and an infinite multiplier
+// is no affine map at all): the tile is then evaluated in sequence instead
+// (seq_tile) and these results are not used.
+template <bool Seg, int kRows>
+__device__ __forceinline__ bool tile_local_scan(const float4 (&va)[kRows],
+                                                const float4 (&vb)[kRows],
+                                                const uint32_t (&hd)[kRows], Map (&im)[kRows],
+                                                Map &wagg) {
+  using Op = AffOp<Seg, false>;
+  using COp = AffOp<Seg, true>;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  bool bad = false;
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
-    float ca = va[r].x, cb = vb[r].x;
-    Op::compose(ca, cb, va[r].y, vb[r].y, ca, cb);
-    Op::compose(ca, cb, va[r].z, vb[r].z, ca, cb);
-    Op::compose(ca, cb, va[r].w, vb[r].w, ca, cb);
-    wave_scan<Op>(ca, cb);
-    ia[r] = ca;
-    ib[r] = cb;
+    Map m = item_map(va[r].x, vb[r].x, hd[r], 0);
+    m = Op::compose(m, item_map(va[r].y, vb[r].y, hd[r], 1));
+    m = Op::compose(m, item_map(va[r].z, vb[r].z, hd[r], 2));
+    m = Op::compose(m, item_map(va[r].w, vb[r].w, hd[r], 3));
+    wave_scan<Op>(m);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(m.a == 0.0f) != 0, 0)) {  // an underflow or a zero
+      const float z = fminf(fminf(fabsf(va[r].x), fabsf(va[r].y)),
+                            fminf(fabsf(va[r].z), fabsf(va[r].w)));
+      const uint64_t zeros = __builtin_amdgcn_ballot_w64(z == 0.0f);
+      const uint64_t upto = ~uint64_t(0) >> (63 - lane);  // lanes 0 .. lane
+      if (m.a == 0.0f && (zeros & upto) == 0) m.a = nudge(m.a);
+    }
+    if constexpr (Seg) {
+      // A head inside the row discards what precedes it from the row's total,
+      // so every lane's prefix is looked at.
+      const bool nf = !__builtin_isfinite(m.a) || !__builtin_isfinite(m.b);
+      bad = bad || __builtin_amdgcn_ballot_w64(nf) != 0;
+    }
+    im[r] = m;
   }
-  float wa = lane_f(ia[0], 63), wb = lane_f(ib[0], 63);
+  // Without heads an inf or NaN anywhere in a row leaves the row's total
+  // non-finite (no IEEE operation of a composition turns it finite again).
+  wagg = lane_map(im[0], 63);
+  bad = bad || uniform_nonfinite(wagg.a) || uniform_nonfinite(wagg.b);
 #pragma unroll
   for (int r = 1; r < kRows; ++r) {
-    const float ra = lane_f(ia[r], 63), rb = lane_f(ib[r], 63);
-    Op::compose(wa, wb, ra, rb, wa, wb);
+    const Map t = lane_map(im[r], 63);
+    bad = bad || uniform_nonfinite(t.a) || uniform_nonfinite(t.b);
+    wagg = COp::compose(wagg, t);
   }
-  if (lane == 0) {
-    s_wave_a[wave] = wa;
-    s_wave_b[wave] = wb;
-  }
+  return bad;
 }
 
 // Data waves, phase 2: carry into each row, then into each lane's chunk, then
 // re-run the recurrence over the lane's 4 items and store (with segments,
 // the last value of each sequence also goes to h_last).
-template <bool Seg, class Op, int kRows = Shape<Seg>::kRows>
+template <bool Seg, int kRows = Shape<Seg>::kRows>
 __device__ __forceinline__ void tile_apply(const float4 (&va)[kRows], const float4 (&vb)[kRows],
-                                           const float (&ia)[kRows], const float (&ib)[kRows],
-                                           float c, float *__restrict__ h, int64_t n,
-                                           int64_t tile, const Segments &sg) {
+                                           const Map (&im)[kRows], float c,
+                                           float *__restrict__ h, int64_t n, int64_t tile,
+                                           const Segments &sg) {
+  using Op = AffOp<Seg, true>;
   constexpr int kWaveElems = Shape<Seg>::kWaveElems, kTileElems = Shape<Seg>::kTileElems;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -376,14 +452,23 @@ __device__ __forceinline__ void tile_apply(const float4 (&va)[kRows], const floa
   const bool full = (tile + 1) * kTileElems <= n;
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
-    const float end = Op::apply(ia[r], c, ib[r]);           // h after this lane's chunk
+    const float end = Op::apply(im[r], c);                  // h after this lane's chunk
     const float cin = dpp<kWaveShr1, 0xf, 0xf>(c, end);     // h before it
-    float4 o;
-    o.x = Op::apply(va[r].x, cin, vb[r].x);
-    o.y = Op::apply(va[r].y, o.x, vb[r].y);
-    o.z = Op::apply(va[r].z, o.y, vb[r].z);
-    o.w = Op::apply(va[r].w, o.z, vb[r].w);
     const int64_t off = wave_start + r * kRowElems + lane * 4;
+    float4 o;
+    o.x = __builtin_fmaf(va[r].x, cin, vb[r].x);
+    o.y = __builtin_fmaf(va[r].y, o.x, vb[r].y);
+    o.z = __builtin_fmaf(va[r].z, o.y, vb[r].z);
+    o.w = __builtin_fmaf(va[r].w, o.z, vb[r].w);
+    if constexpr (Seg) {
+      const uint32_t hb = seg_heads(off, n, sg);
+      if (hb) {  // a head ignores the value before it
+        o.x = (hb & 1u) ? vb[r].x : o.x;
+        o.y = (hb & 2u) ? vb[r].y : __builtin_fmaf(va[r].y, o.x, vb[r].y);
+        o.z = (hb & 4u) ? vb[r].z : __builtin_fmaf(va[r].z, o.y, vb[r].z);
+        o.w = (hb & 8u) ? vb[r].w : __builtin_fmaf(va[r].w, o.z, vb[r].w);
+      }
+    }
     if (full) {
       store_nt(h + off, o);
     } else {
@@ -442,7 +527,7 @@ __device__ __forceinline__ int64_t successor(int64_t t, int64_t ntiles, const Li
   return claim_tile(st, ntiles, lane).tile;
 }
 
-// Called by every wave as it finishes. Epochs are 32-bit, so after a full
+// Called by every wave as it finishes. Epochs are 31-bit, so after a full
 // cycle a status word left from the previous pass over the epochs could look
 // current; the launch that takes the cycle's last epoch therefore counts its
 // waves out (acquire-release, so every status access of the launch comes
@@ -471,13 +556,15 @@ __device__ __forceinline__ void check_out(const LinearStatus &st, uint32_t epoch
 template <bool Seg>
 struct Shared {
   static constexpr int kWaves = Shape<Seg>::kWaves, kRows = Shape<Seg>::kRows;
-  float4 park[2][kWaves][kRows][2][64];        // a, b rows of two parked tiles
-  float wave_a[4][kWaves], wave_b[4][kWaves];  // per-wave aggregates
-  float tile_a[4], tile_b[4];                  // tile aggregates
-  float carry[4][kWaves];                      // h entering each wave's rows
-  int64_t ids[4];                              // claimed tiles, in claim order
-  unsigned arrived[2];                         // data waves done with a tile's local scan
-  uint32_t epoch;                              // this launch's epoch
+  float4 park[2][kWaves][kRows][2][64];  // a, b rows of two parked tiles
+  Map wave[4][kWaves];                   // per-wave aggregates
+  Map tile[4];                           // tile aggregates
+  uint32_t wave_seq[4][kWaves];          // the wave's rows hold an inf or NaN
+  uint32_t tile_seq[4];                  // so does the tile: evaluated in sequence (seq_tile)
+  float carry[4][kWaves];                // h entering each wave's rows
+  int64_t ids[4];                        // claimed tiles, in claim order
+  unsigned arrived[2];                   // data waves done with a tile's local scan
+  uint32_t epoch;                        // this launch's epoch
 };
 
 template <bool Seg, int kRows = Shape<Seg>::kRows>
@@ -503,34 +590,92 @@ __device__ __forceinline__ void unpark(const Shared<Seg> &sh, int slot, float4 (
   }
 }
 
+// A tile holding an inf or NaN is evaluated element by element, in sequence
+// order, from its exact incoming value h_in, by one lane of the control wave
+// from the a/b parked in LDS: that gives the sequential loop's IEEE results
+// exactly. A parallel scan cannot in general: it multiplies multipliers, and
+// a multiplier of +-inf makes the state after it depend on the sign of the
+// state before it, which no affine map of the incoming value expresses (a
+// composition forms inf*x + inf*y where the loop forms inf*(x + y)). The
+// function writes the tile's outputs (and, with segments, h_last) and
+// returns the value after the tile's last element; the tile is then
+// published as a constant map (a head) with that value, so later tiles see
+// exactly the loop's state. Only inputs holding inf or NaN take this path.
+template <bool Seg>
+__device__ __forceinline__ float seq_tile(const Shared<Seg> &sh, int slot, int64_t tile, float h_in,
+                          float *__restrict__ h, int64_t n, const Segments &sg) {
+  constexpr int kWaves = Shape<Seg>::kWaves, kRows = Shape<Seg>::kRows,
+                kTileElems = Shape<Seg>::kTileElems;
+  float v = h_in;
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll 1
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll 1
+      for (int r = 0; r < kRows; ++r)
+#pragma unroll 1
+        for (int l = 0; l < 64; ++l) {
+          const float4 av = sh.park[slot][w][r][0][l], bv = sh.park[slot][w][r][1][l];
+          const float ta[4] = {av.x, av.y, av.z, av.w}, tb[4] = {bv.x, bv.y, bv.z, bv.w};
+          const int64_t off = tile * kTileElems + int64_t(w) * Shape<Seg>::kWaveElems +
+                              r * kRowElems + l * 4;
+          for (int j = 0; j < 4; ++j) {
+            if (off + j >= n) continue;
+            bool head = false;
+            uint32_t k = 0, t = 1;
+            if constexpr (Seg) {
+              seg_pos(uint32_t(off + j), sg, k, t);
+              head = t == 0;
+            }
+            v = head ? tb[j] : __builtin_fmaf(ta[j], v, tb[j]);
+            h[off + j] = v;
+            if constexpr (Seg) {
+              if (sg.h_last && t == sg.len - 1) sg.h_last[k] = v;
+            }
+          }
+        }
+  }
+  return lane_f(v, 0);
+}
+
 // Data waves: local scan of a loaded tile; the last data wave to finish folds
 // the wave aggregates into the tile aggregate and publishes it (level 0) at
 // once, without waiting for any other workgroup.
-template <class Op, bool Seg, int kRows = Shape<Seg>::kRows>
+template <bool Seg, int kRows = Shape<Seg>::kRows>
 __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
-                                                 const float4 (&vb)[kRows], float (&ia)[kRows],
-                                                 float (&ib)[kRows], Shared<Seg> &sh, int ring,
-                                                 int slot, const LinearStatus &st, int64_t tile,
+                                                 const float4 (&vb)[kRows],
+                                                 const uint32_t (&hd)[kRows], Map (&im)[kRows],
+                                                 Shared<Seg> &sh, int ring, int slot,
+                                                 const LinearStatus &st, int64_t tile,
                                                  uint32_t epoch) {
+  using COp = AffOp<Seg, true>;
   constexpr int kWaves = Shape<Seg>::kWaves;
   const int lane = threadIdx.x & 63;
-  tile_local_scan<Op, kRows>(va, vb, ia, ib, sh.wave_a[ring], sh.wave_b[ring]);
+  const int wave = threadIdx.x >> 6;
+  Map wagg;
+  const uint32_t seq = tile_local_scan<Seg, kRows>(va, vb, hd, im, wagg) ? 1u : 0u;
+  if (lane == 0) {
+    sh.wave[ring][wave] = wagg;
+    sh.wave_seq[ring][wave] = seq;
+  }
   unsigned prior = 0;
   if (lane == 0)
     prior = __hip_atomic_fetch_add(&sh.arrived[slot], 1u, __ATOMIC_ACQ_REL,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
   prior = __builtin_amdgcn_readfirstlane(prior);
   if (prior == kWaves - 1) {
-    float ga = sh.wave_a[ring][0], gb = sh.wave_b[ring][0];
+    Map g = sh.wave[ring][0];
+    uint32_t seq = sh.wave_seq[ring][0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      Op::compose(ga, gb, sh.wave_a[ring][w], sh.wave_b[ring][w], ga, gb);
+      g = COp::compose(g, sh.wave[ring][w]);
+      seq |= sh.wave_seq[ring][w];
     }
     if (lane == 0) {
-      st_status(&st.lvl0[tile].a, epoch, ga);
-      st_status(&st.lvl0[tile].b, epoch, gb);
-      sh.tile_a[ring] = ga;
-      sh.tile_b[ring] = gb;
+      // A tile evaluated in sequence is published by the control wave once
+      // it has its value (see seq_tile).
+      if (!seq) st_map(st.lvl0[tile], epoch, g);
+      sh.tile[ring] = g;
+      sh.tile_seq[ring] = seq;
       sh.arrived[slot] = 0;  // reused two tiles later, after two barriers
     }
   }
@@ -578,7 +723,10 @@ template <bool Seg>
 __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
     const float *__restrict__ a, const float *__restrict__ b, float h0,
     float *__restrict__ h, int64_t n, int64_t ntiles, LinearStatus st, Segments sg) {
-  using Op = typename std::conditional<Seg, ResetOp, PlainOp>::type;
+  using COp = AffOp<Seg, true>;
+  // The control wave's compositions honour heads in both forms: a tile with
+  // an infinite multiplier is published as one (see seq_tile).
+  using HOp = AffOp<true, true>;
   constexpr int kWaves = Shape<Seg>::kWaves, kRows = Shape<Seg>::kRows;
   __shared__ Shared<Seg> sh;
   const int lane = threadIdx.x & 63;
@@ -622,13 +770,19 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
           lb_check(lp, epoch);
         }
         const int rp = (j - 1) & 3;
-        const Prefix pf = lb_finish<Op>(lp, h0, lane);
-        publish_higher<Op>(st, tp, pf, sh.tile_a[rp], sh.tile_b[rp], epoch, lane);
-        if (lane == 0) {
-          float c = pf.h_in;
-          for (int w = 0; w < kWaves; ++w) {
-            sh.carry[rp][w] = c;
-            c = Op::apply(sh.wave_a[rp][w], c, sh.wave_b[rp][w]);
+        const Prefix pf = lb_finish<HOp, Seg>(lp, h0, lane);
+        if (__builtin_expect(sh.tile_seq[rp] != 0, 0)) {  // rare: an inf or NaN in the tile
+          const Map own{0.0f, seq_tile<Seg>(sh, (j - 1) & 1, tp, pf.h_in, h, n, sg), 1u};
+          if (lane == 0) st_map(st.lvl0[tp], epoch, own);
+          publish_higher<HOp>(st, tp, pf, own, epoch, lane);
+        } else {
+          publish_higher<HOp>(st, tp, pf, sh.tile[rp], epoch, lane);
+          if (lane == 0) {
+            float c = pf.h_in;
+            for (int w = 0; w < kWaves; ++w) {
+              sh.carry[rp][w] = c;
+              c = COp::apply(sh.wave[rp][w], c);
+            }
           }
         }
       }
@@ -656,15 +810,16 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
   // Register stages: (va, vb) tile being applied, (na, nb) tile being
   // scanned, (ma, mb) tile being loaded; prefixes of the two parked tiles.
   float4 va[kRows], vb[kRows], na[kRows], nb[kRows];
-  float iap[kRows], ibp[kRows], iaw[kRows], ibw[kRows];
-  if (t0 < ntiles) load_tile<Seg>(a, b, n, t0, sg, va, vb);
+  uint32_t hv[kRows], hn[kRows];
+  Map imp[kRows], imw[kRows];
+  if (t0 < ntiles) load_tile<Seg>(a, b, n, t0, sg, va, vb, hv);
   __syncthreads();  // A1
   int64_t t1 = sh.ids[1];
-  if (t1 < ntiles) load_tile<Seg>(a, b, n, t1, sg, na, nb);
+  if (t1 < ntiles) load_tile<Seg>(a, b, n, t1, sg, na, nb, hn);
   __syncthreads();  // A
   int64_t t2 = sh.ids[2];
   if (t0 < ntiles) {
-    scan_and_publish<Op, Seg>(va, vb, iaw, ibw, sh, 0, 0, st, t0, epoch);
+    scan_and_publish<Seg>(va, vb, hv, imw, sh, 0, 0, st, t0, epoch);
     park(sh, 0, va, vb);
   }
   __syncthreads();  // B
@@ -673,25 +828,25 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
     int64_t claimed = ntiles;
     if (wave == 0 && t2 < ntiles) claimed = successor(t2, ntiles, st, lane);
     float4 ma[kRows], mb[kRows];
-    if (t2 < ntiles) load_tile<Seg>(a, b, n, t2, sg, ma, mb);
-    float nia[kRows], nib[kRows];
+    uint32_t hm[kRows];
+    if (t2 < ntiles) load_tile<Seg>(a, b, n, t2, sg, ma, mb, hm);
+    Map nim[kRows];
     if (t1 < ntiles)
-      scan_and_publish<Op, Seg>(na, nb, nia, nib, sh, (j + 1) & 3, (j + 1) & 1, st, t1, epoch);
+      scan_and_publish<Seg>(na, nb, hn, nim, sh, (j + 1) & 3, (j + 1) & 1, st, t1, epoch);
     if (wave == 0 && lane == 0) sh.ids[(j + 3) & 3] = claimed;
     __syncthreads();  // C_j
-    if (tp < ntiles) {
+    if (tp < ntiles && __builtin_expect(sh.tile_seq[(j - 1) & 3] == 0, 1)) {  // else the control wave wrote it
       unpark(sh, (j + 1) & 1, va, vb);  // t_{j-1} sits in slot (j - 1) % 2
-      tile_apply<Seg, Op>(va, vb, iap, ibp, sh.carry[(j - 1) & 3][wave], h, n, tp, sg);
+      tile_apply<Seg>(va, vb, imp, sh.carry[(j - 1) & 3][wave], h, n, tp, sg);
     }
     if (t1 < ntiles) park(sh, (j + 1) & 1, na, nb);
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      iap[r] = iaw[r];
-      ibp[r] = ibw[r];
-      iaw[r] = nia[r];
-      ibw[r] = nib[r];
+      imp[r] = imw[r];
+      imw[r] = nim[r];
       na[r] = ma[r];
       nb[r] = mb[r];
+      hn[r] = hm[r];
     }
     tp = t0;
     t0 = t1;

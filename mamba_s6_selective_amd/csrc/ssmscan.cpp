@@ -37,12 +37,23 @@ bool overlap(const void *p, size_t pb, const void *q, size_t qb) {
 struct LinearWorkspace {
   AggWord *words = nullptr;  // counters and the three status levels (see linear_workspace)
   int64_t capacity = 0;      // tiles
+  uint32_t epoch_cycle = 0;  // fixed when the words are created
 };
 
 static_assert(LinearStatus::kDoneOffset * sizeof(unsigned long long) == 128,
               "the done count sits 128 bytes into the 256-byte counter header");
-constexpr uint32_t kDefaultEpochCycle = 0xffffffffu;
-uint32_t g_epoch_cycle = kDefaultEpochCycle;
+// Epochs are 31-bit (bit 31 of a status word's high half is the batched
+// scan's head flag). SSMSCAN_LINEAR_EPOCH_CYCLE, read when a workspace is
+// created, shortens the cycle so that tests can exercise the clearing.
+constexpr uint32_t kDefaultEpochCycle = 0x7fffffffu;
+
+uint32_t epoch_cycle_for_new_workspace() {
+  if (const char *env = getenv("SSMSCAN_LINEAR_EPOCH_CYCLE")) {
+    const long long v = atoll(env);
+    if (v >= 1 && v <= (long long)kDefaultEpochCycle) return uint32_t(v);
+  }
+  return kDefaultEpochCycle;
+}
 
 struct S6Workspace {
   void *buf = nullptr;
@@ -146,6 +157,7 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
     }
     ws.words = static_cast<AggWord *>(p);
     ws.capacity = cap;
+    ws.epoch_cycle = epoch_cycle_for_new_workspace();
   }
   char *base = reinterpret_cast<char *>(ws.words);
   status->claims = reinterpret_cast<unsigned long long *>(base);  // done count at +128
@@ -153,7 +165,7 @@ static int linear_workspace(hipStream_t stream, int64_t ntiles, LinearStatus *st
   status->lvl1 = reinterpret_cast<AggWord *>(base + 256 + pad(ws.capacity));
   status->lvl2 = reinterpret_cast<AggWord *>(base + 256 + pad(ws.capacity) + pad(ws.capacity / 64));
   status->nwords = (bytes_for(ws.capacity) - 256) / int64_t(sizeof(uint64_t));
-  status->epoch_cycle = g_epoch_cycle;
+  status->epoch_cycle = ws.epoch_cycle;
   return SSM_OK;
 }
 
@@ -406,18 +418,6 @@ const char *ssm_status_string(int code) {
 }
 
 const char *ssm_last_error(void) { return g_last_error.c_str(); }
-
-int ssm_linear_scan_set_epoch_cycle(uint32_t cycle) {
-  g_last_error.clear();
-  if (cycle == 0) return fail(SSM_ERR_INVALID_ARG, "cycle must be >= 1");
-  std::lock_guard<std::mutex> lock(g_mu);
-  for (auto &kv : g_linear)
-    if (kv.second.words)
-      return fail(SSM_ERR_INVALID_ARG,
-                  "a linear-scan workspace exists; call ssm_release_workspace first");
-  g_epoch_cycle = cycle;
-  return SSM_OK;
-}
 
 int ssm_release_workspace(void) {
   g_last_error.clear();

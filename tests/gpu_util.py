@@ -37,3 +37,24 @@ def assert_close(got, ref, tol, what=""):
     err = max_scaled_err(got, ref)
     say(f"  {what}: max |err|/(1+|ref|) = {err:.3e} (tol {tol:g})")
     assert err <= tol, f"{what}: {err} > {tol}"
+
+
+def assert_same_nonfinite(got, ref, tol, what=""):
+    """Element by element against the oracle with non-finite values included:
+    NaN where the oracle has NaN, +inf / -inf where it has +inf / -inf (sign
+    included), and the finite values within tol * (1 + |ref|)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    for name, fn in (("NaN", np.isnan), ("+inf", np.isposinf), ("-inf", np.isneginf)):
+        g, r = fn(got), fn(ref)
+        if not np.array_equal(g, r):
+            bad = np.flatnonzero(g != r)
+            raise AssertionError(
+                f"{what}: {name} positions differ at {bad.size} elements, first "
+                f"{bad[:5].tolist()} (got {got.ravel()[bad[:5]].tolist()}, "
+                f"oracle {ref.ravel()[bad[:5]].tolist()})")
+    m = np.isfinite(ref)
+    err = float(np.max(np.abs(got[m] - ref[m]) / (1.0 + np.abs(ref[m])))) if m.any() else 0.0
+    say(f"  {what}: {int((~m).sum())} non-finite matched, finite max err {err:.3e}")
+    assert err <= tol, f"{what}: {err} > {tol}"

@@ -176,15 +176,3 @@ def test_outputs_overlapping_inputs_are_rejected():
     for fn in (lib.ssm_selective_scan_fwd, lib.ssm_selective_scan_fwd_bf16):
         assert fn(*bad, 1, 10, 8, 16, 0, None) == ssm.SSM_ERR_INVALID_ARG
         assert b"overlaps" in lib.ssm_last_error()
-
-
-def test_epoch_cycle_setter_argument_errors():
-    lib = ssm.load_library()
-    assert lib.ssm_linear_scan_set_epoch_cycle(0) == -1
-    with pytest.raises(ValueError):
-        ssm.linear_scan_set_epoch_cycle(0)
-    with pytest.raises(ValueError):
-        ssm.linear_scan_set_epoch_cycle(2**32)
-    # No workspace exists in a process that has made no GPU call.
-    assert lib.ssm_linear_scan_set_epoch_cycle(7) == 0
-    assert lib.ssm_linear_scan_set_epoch_cycle(2**32 - 1) == 0

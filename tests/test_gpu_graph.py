@@ -5,6 +5,8 @@ replays, equals the eager result bit for bit. The single-pass linear scans
 take their status-word epoch from the device, so replays and eager calls on
 the same workspace keep getting fresh epochs; a short epoch cycle drives the
 clearing of the status words that ends each cycle through many wraps."""
+import os
+
 import pytest
 import torch
 
@@ -137,7 +139,7 @@ def test_linear_epoch_cycle_clears_status_words():
         for cycle in (3, 2, 1):
             say(f"linear epoch cycle {cycle}")
             ssm.release_workspace()
-            ssm.linear_scan_set_epoch_cycle(cycle)
+            os.environ["SSMSCAN_LINEAR_EPOCH_CYCLE"] = str(cycle)  # read by new workspaces
             outs = [(k, calls[k]()) for k in seq]
             torch.cuda.synchronize()
             for i, (k, h) in enumerate(outs):
@@ -167,7 +169,7 @@ def test_linear_epoch_cycle_clears_status_words():
                 del g
     finally:
         ssm.release_workspace()
-        ssm.linear_scan_set_epoch_cycle(2**32 - 1)
+        os.environ.pop("SSMSCAN_LINEAR_EPOCH_CYCLE", None)
 
 
 def test_workspace_growth_during_capture_is_refused():

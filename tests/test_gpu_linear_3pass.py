@@ -95,3 +95,34 @@ def test_3pass_full_size_workload_and_determinism():
     torch.cuda.synchronize()
     ref = native.linear_scan(a.numpy(), b.numpy(), 0.0)
     assert_close(first.cpu().numpy(), ref, TOL, "linear-n134217728 3-pass")
+
+
+@pytest.mark.parametrize("kind", sorted(KINDS))
+def test_3pass_above_2_27_uncached_carry_exact(kind):
+    """n = 2^28 + 5*8192 + 3: more than 16384 tiles, so the carry pass's
+    waves hold more than one batch of 16 rows and re-scan them on the second
+    walk, and the last tile is ragged. a = 1 and b = 1 at 1000 seeded
+    positions (0 elsewhere): h[i] = h0 + (ones at positions <= i) exactly in
+    fp32 whatever the grouping. Checked at every tile end, at the ones and
+    just before them, at the last element and at 2^20 seeded positions."""
+    n = (1 << 28) + 5 * 8192 + 3
+    say(f"{kind} n={n}: a = 1, sparse integer b")
+    dev = need_gpu()
+    g = torch.Generator().manual_seed(2028)
+    pos = np.unique(torch.randint(0, n, (1000,), generator=g).numpy().astype(np.int64))
+    a = torch.ones(n, device=dev)
+    b = torch.zeros(n, device=dev)
+    b[torch.from_numpy(pos).to(dev)] = 1.0
+    h = KINDS[kind](a, b, 0.5)
+    del a, b
+    tile = 8192
+    idx = np.concatenate([
+        np.arange(tile - 1, n, tile, dtype=np.int64), [0, n - 1], pos, np.maximum(pos - 1, 0),
+        torch.randint(0, n, (1 << 20,), generator=g).numpy().astype(np.int64)])
+    got = h[torch.from_numpy(idx).to(dev)].cpu().numpy()
+    del h
+    torch.cuda.synchronize()
+    expected = 0.5 + np.searchsorted(pos, idx, side="right").astype(np.float64)
+    bad = int(np.count_nonzero(got != expected))
+    say(f"  {idx.size} positions checked, {bad} differ")
+    assert bad == 0

@@ -1,0 +1,141 @@
+"""Non-finite inputs: every linear scan (single-pass, three-pass, Hillis-Steele
+and batched) against the float64 oracle element by element, with NaN and
++-inf positions (and signs) compared exactly.
+
+The sequential loop h = a*h + b never multiplies multipliers together; the
+scans do, and a long product of multipliers below 1 underflows in fp32. The
+cases plant inf/NaN in b, h0 and a, exact zeros after an infinite state, and
+place them at the first element, inside rows, at row, wave and tile ends, in
+later superblocks and in the ragged last tile, with a ~ U(0.5, 1) so that
+products over a tile underflow.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mamba_s6_selective_amd as ssm
+from gpu_util import assert_same_nonfinite, need_gpu, say
+from mamba_s6_selective_amd.workloads import linear_inputs
+from oracle import native
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+INF, NAN = float("inf"), float("nan")
+N = 300 * 8192 + 77          # 301 tiles of the single-pass and three-pass scans: level-1 windows
+POS = [0, 5, 1023, 8191, 64 * 8192 + 300, N - 1]   # first, in a row, wave end, tile end, later, last
+
+# name -> list of (array, offset into POS or absolute position, value), h0
+CASES = {
+    "b+inf": ([("b", 0, INF)], 0.0),
+    "b-inf": ([("b", 0, -INF)], 0.0),
+    "bnan": ([("b", 0, NAN)], 0.0),
+    "b+inf then b-inf": ([("b", 0, INF), ("b", 7777, -INF)], 0.0),
+    "b+inf then a=0": ([("b", 0, INF), ("a", 9000, 0.0)], 0.0),
+    "a+inf": ([("a", 0, INF)], 0.5),
+    "a-inf": ([("a", 0, -INF)], 0.5),
+    "anan": ([("a", 0, NAN)], 0.5),
+    "a=0 then a+inf": ([("a", 0, 0.0), ("a", 3000, INF)], 0.5),
+    "two a+inf": ([("a", 0, INF), ("a", 20000, -INF)], 0.5),
+}
+
+
+def planted(case, p, n=N, seed=4242):
+    a, b = linear_inputs(n, seed=seed, a_lo=0.5, a_hi=1.0)
+    plants, h0 = CASES[case]
+    for arr, delta, v in plants:
+        i = min(p + delta, n - 1)
+        (a if arr == "a" else b)[i] = v
+    return a, b, h0
+
+
+SCANS = {"single": ssm.linear_scan, "3pass": ssm.linear_scan_3pass, "hs": ssm.linear_scan_hs}
+
+
+@pytest.mark.parametrize("scan", sorted(SCANS))
+@pytest.mark.parametrize("p", POS)
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_nonfinite_linear(case, p, scan):
+    say(f"nonfinite {scan}: {case} at {p}")
+    dev = need_gpu()
+    a, b, h0 = planted(case, p)
+    h = SCANS[scan](a.to(dev), b.to(dev), h0).cpu().numpy()
+    ref = native.linear_scan(a.numpy(), b.numpy(), h0)
+    assert_same_nonfinite(h, ref, TOL, f"{scan} {case}@{p}")
+
+
+@pytest.mark.parametrize("scan", sorted(SCANS))
+@pytest.mark.parametrize("h0", [INF, -INF, NAN])
+def test_nonfinite_h0(scan, h0):
+    say(f"nonfinite {scan}: h0 = {h0}")
+    dev = need_gpu()
+    a, b = linear_inputs(70 * 8192 + 5, seed=11, a_lo=0.5, a_hi=1.0)
+    h = SCANS[scan](a.to(dev), b.to(dev), h0).cpu().numpy()
+    ref = native.linear_scan(a.numpy(), b.numpy(), h0)
+    assert_same_nonfinite(h, ref, TOL, f"{scan} h0={h0}")
+
+
+@pytest.mark.parametrize("scan", sorted(SCANS))
+def test_nonfinite_small_multipliers_everywhere(scan):
+    """a ~ U(0, 0.01): products underflow within a few elements everywhere;
+    an inf in b must stay inf through them (and later NaN from an exact 0)."""
+    dev = need_gpu()
+    n = 40 * 8192 + 3
+    a, b = linear_inputs(n, seed=12, a_lo=0.0, a_hi=0.01)
+    b[1234] = INF
+    b[5 * 8192 + 17] = -INF
+    a[20 * 8192] = 0.0
+    b[30 * 8192 + 1] = NAN
+    h = SCANS[scan](a.to(dev), b.to(dev), 0.25).cpu().numpy()
+    ref = native.linear_scan(a.numpy(), b.numpy(), 0.25)
+    assert_same_nonfinite(h, ref, TOL, f"{scan} small a")
+
+
+@pytest.mark.parametrize("scan", sorted(SCANS))
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 257, 8193])
+def test_nonfinite_tiny_sizes(scan, n):
+    dev = need_gpu()
+    for case in ("b+inf", "a-inf", "bnan"):
+        a, b, h0 = planted(case, n // 2, n=n, seed=n)
+        h = SCANS[scan](a.to(dev), b.to(dev), h0).cpu().numpy()
+        ref = native.linear_scan(a.numpy(), b.numpy(), h0)
+        assert_same_nonfinite(h, ref, TOL, f"{scan} n={n} {case}")
+
+
+# batched: shapes with long sequences (several tiles each), many short ones
+# per tile, and length-1 sequences
+BATCHED = [(24, 40000), (500, 1000), (3000, 3), (9, 8448 * 3 + 1)]
+
+
+@pytest.mark.parametrize("shape", BATCHED, ids=[f"{s[0]}x{s[1]}" for s in BATCHED])
+def test_nonfinite_batched_all_sequences(shape):
+    """inf / NaN in b, h0 and a inside some sequences, at their first and
+    last elements and in between; every sequence, those holding the values
+    included, against the oracle run on that sequence alone, and h_last."""
+    nseq, length = shape
+    say(f"nonfinite batched {nseq} x {length}")
+    dev = need_gpu()
+    g = torch.Generator().manual_seed(nseq + length)
+    a = 0.5 + 0.5 * torch.rand(nseq, length, generator=g)
+    b = torch.randn(nseq, length, generator=g)
+    h0 = torch.randn(nseq, generator=g)
+    mid = length // 2
+    b[1, mid] = INF                        # inf inside a sequence
+    h0[2] = INF                            # an infinite start
+    h0[3] = NAN
+    b[4, 0] = -INF                         # at a sequence's first element
+    b[5, length - 1] = NAN                 # at its last: the next one is unaffected
+    a[6, mid] = INF                        # an infinite multiplier
+    b[7, 0] = INF
+    if length > 1:
+        a[7, length - 1] = 0.0             # then an exact zero: NaN
+        a[0, length - 1] = -INF            # at a last element, sequence 0
+    if nseq > 100:
+        b[100, mid] = -INF
+        a[101, 0] = INF                    # infinite multiplier at a first element
+    h, last = ssm.linear_scan_batched(a.to(dev), b.to(dev), h0.to(dev))
+    h, last = h.cpu().numpy(), last.cpu().numpy()
+    ref = np.stack([native.linear_scan(a[k].numpy(), b[k].numpy(), float(h0[k]))
+                    for k in range(nseq)])
+    assert_same_nonfinite(h, ref, TOL, f"batched {nseq}x{length}")
+    assert_same_nonfinite(last, ref[:, -1], TOL, "h_last")
+    assert np.array_equal(last, h[:, -1], equal_nan=True)  # the same values, bit for bit
