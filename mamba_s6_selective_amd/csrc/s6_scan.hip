@@ -54,6 +54,23 @@ __device__ __forceinline__ float ldv(const uint16_t *p) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x with zero kept for x = -inf only. v_exp_f32 flushes results below 2^-126
+// to zero; a state of +-inf multiplied by that zero would give NaN where the
+// exact (tiny, non-zero) factor keeps it infinite, as the float64 recurrence
+// does. Such a result becomes the smallest subnormal instead (for a finite
+// state that changes the product by at most 2^-149 times the state).
+__device__ __forceinline__ float exp2_nz(float x) {
+  const float e = exp2_hw(x);
+  return (e == 0.0f && x > -__builtin_inff()) ? __uint_as_float(1u) : e;
+}
+// x*y for factors that are non-negative or NaN (products of exponentials):
+// a zero from two non-zero factors (an underflow) becomes the smallest
+// subnormal, so "exactly zero" keeps meaning "a factor was exactly zero".
+__device__ __forceinline__ float mul_pos_nz(float x, float y) {
+  const float p = x * y;
+  return (p == 0.0f && x != 0.0f && y != 0.0f) ? __uint_as_float(1u) : p;
+}
+
 // Waits for every outstanding scalar (and LDS) load. Scalar loads may return
 // out of order, so a wait for one row is a wait for all; issuing it before the
 // next step's row loads (rather than letting the compiler place it after them)
@@ -173,7 +190,7 @@ __device__ __forceinline__ DX make_dx(const float *bias, int d) {
 }
 
 // One step of the chunk-local recurrence for one lane: returns y's value.
-template <typename T, int NT>
+template <typename T, int NT, bool Careful = false>
 __device__ __forceinline__ float s6_step(float dt, float x, const Row<T, NT> &Br,
                                          const Row<T, NT> &Cr, const float (&Ap)[NT],
                                          float Dd, float (&h)[NT]) {
@@ -182,7 +199,7 @@ __device__ __forceinline__ float s6_step(float dt, float x, const Row<T, NT> &Br
   float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    const float dA = exp2_hw(dt * Ap[n]);
+    const float dA = Careful ? exp2_nz(dt * Ap[n]) : exp2_hw(dt * Ap[n]);
     h[n] = __builtin_fmaf(dA, h[n], du * Br.get(n));
     if (n & 1)
       acc1 = __builtin_fmaf(Cr.get(n), h[n], acc1);
@@ -250,6 +267,9 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
 #pragma unroll
   for (int n = 0; n < NT; ++n) h[n] = 0.0f;
   S = 0.0f;
+  float ap_min = Ap[0];  // the most negative exponent factor of the lane
+#pragma unroll
+  for (int n = 1; n < NT; ++n) ap_min = fminf(ap_min, Ap[n]);
   const size_t row0 = size_t(b) * g.L;
   const int len = t1 - t0;
   const int full = len - len % kPrefetch;
@@ -306,32 +326,59 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
       }
       touched = touch_rows<T, NT>(B, C, block_row(i0 + kPrefetch) * NT);
     }
-    // B/C rows go one step ahead: step j's rows were loaded during step j-1.
-    Row<T, NT> Bc, Cc;
-    Bc.load(B + (row0 + tof(i0)) * NT);
-    Cc.load(C + (row0 + tof(i0)) * NT);
     float smin = 0.0f, ymin = 0.0f;
+    // A step's exponential can flush to zero only if delta*A*log2(e) < -126
+    // (|delta*A| > 87); decided per block from the largest delta (an infinite
+    // one included). Such a block runs step by step with exp2_nz, so that an
+    // infinite state stays infinite as in the float64 recurrence: a compact
+    // loop that reads its words again (a second unrolled copy of the block
+    // spilled registers in the common path).
+    float dmax = cd[0];
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
-      Row<T, NT> Bn, Cn;
-      wait_scalar_loads();
-      if (j + 1 < kPrefetch) {
-        Bn.load(B + (row0 + tof(i0 + j + 1)) * NT);
-        Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
+    for (int j = 1; j < kPrefetch; ++j) dmax = fmaxf(dmax, cd[j]);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(dmax * ap_min < -126.0f) != 0, 0)) {
+#pragma unroll 1
+      for (int j = 0; j < kPrefetch; ++j) {
+        const size_t r = row(i0 + j);
+        const float dt = dx(ldv(&at(delta + r, io)));
+        Row<T, NT> Bc, Cc;
+        Bc.load(B + (row0 + tof(i0 + j)) * NT);
+        Cc.load(C + (row0 + tof(i0 + j)) * NT);
+        const float out = s6_step<T, NT, true>(dt, ldv(&at(u + r, io)), Bc, Cc, Ap, Dd, h);
+        float &yr = at(y + r, yo);
+        const float yv = Accumulate ? yr + out : out;
+        yr = yv;
+        S += dt;
+        smin = j == 0 ? S : fminf(smin, S);
+        ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
       }
-      // Keeps the next rows' loads at the head of the step: left to itself the
-      // scheduler may sink them (with their address arithmetic) to just before
-      // the next wait, which then waits for the whole scalar-load latency.
-      __builtin_amdgcn_sched_barrier(0);
-      const float out = s6_step<T, NT>(cd[j], cx[j], Bc, Cc, Ap, Dd, h);
-      const float yv = Accumulate ? cy[j] + out : out;
-      at(y + row(i0 + j), yo) = yv;
-      S += cd[j];
-      smin = j == 0 ? S : fminf(smin, S);
-      ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
-      if (j + 1 < kPrefetch) {
-        Bc = Bn;
-        Cc = Cn;
+    } else {
+      // B/C rows go one step ahead: step j's rows were loaded during step j-1.
+      Row<T, NT> Bc, Cc;
+      Bc.load(B + (row0 + tof(i0)) * NT);
+      Cc.load(C + (row0 + tof(i0)) * NT);
+#pragma unroll
+      for (int j = 0; j < kPrefetch; ++j) {
+        Row<T, NT> Bn, Cn;
+        wait_scalar_loads();
+        if (j + 1 < kPrefetch) {
+          Bn.load(B + (row0 + tof(i0 + j + 1)) * NT);
+          Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
+        }
+        // Keeps the next rows' loads at the head of the step: left to itself the
+        // scheduler may sink them (with their address arithmetic) to just before
+        // the next wait, which then waits for the whole scalar-load latency.
+        __builtin_amdgcn_sched_barrier(0);
+        const float out = s6_step<T, NT>(cd[j], cx[j], Bc, Cc, Ap, Dd, h);
+        const float yv = Accumulate ? cy[j] + out : out;
+        at(y + row(i0 + j), yo) = yv;
+        S += cd[j];
+        smin = j == 0 ? S : fminf(smin, S);
+        ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
+        if (j + 1 < kPrefetch) {
+          Bc = Bn;
+          Cc = Cn;
+        }
       }
     }
     if (stats) {  // wave-uniform
@@ -359,7 +406,7 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
     Row<T, NT> Bc, Cc;
     Bc.load(B + (row0 + t) * NT);
     Cc.load(C + (row0 + t) * NT);
-    const float out = s6_step<T, NT>(dt, x, Bc, Cc, Ap, Dd, h);
+    const float out = s6_step<T, NT, true>(dt, x, Bc, Cc, Ap, Dd, h);
     float &yr = at(y + r, yo);
     yr = Accumulate ? yr + out : out;
     S += dt;
@@ -367,7 +414,7 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
 }
 
 template <typename T, int NT, class DX>
-__global__ __launch_bounds__(kThreads) void s6_chunk_kernel(
+__global__ __launch_bounds__(kThreads, 4) void s6_chunk_kernel(
     const T *__restrict__ u, const T *__restrict__ delta, const float *__restrict__ dbias,
     const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
@@ -469,7 +516,7 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
 #pragma unroll
   for (int i = 0; i < kCarryPart; ++i) {
     const bool in = valid && k0 + i < g.nchunks;  // chunks past the end act as identity maps
-    ra[i] = in ? exp2_hw(Ap * ra[i]) : 1.0f;
+    ra[i] = in ? exp2_nz(Ap * ra[i]) : 1.0f;
     rf[i] = in && fwd ? rf[i] : 0.0f;
     rr[i] = in && rev ? rr[i] : 0.0f;
   }
@@ -478,7 +525,7 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
   for (int i = 0; i < kCarryPart; ++i) {
     tf = __builtin_fmaf(ra[i], tf, rf[i]);
     tr = __builtin_fmaf(ra[kCarryPart - 1 - i], tr, rr[kCarryPart - 1 - i]);
-    ta *= ra[i];
+    ta = mul_pos_nz(ta, ra[i]);
   }
   s_a[part][lane] = ta;
   s_f[part][lane] = tf;
@@ -571,7 +618,11 @@ struct FixGroups {
 #pragma unroll
       for (int g = 0; g < kCount; ++g) bound = fmaf(cabs[g], exp2_hw(p[g]), bound);
       const float t = bound * cscale;
-      const float thr = (sane && !any_keep && t == t) ? fmaxf(t, kTinyY) : __builtin_inff();
+      // The bound holds only for a non-negative running sum: with Ap < 0,
+      // 2^(Ap*S) is largest at the smallest S, and for S < 0 at the most
+      // negative Ap, not at Ag. (A negative sum needs a negative delta.)
+      const float thr =
+          (sane && !any_keep && t == t && smin >= 0.0f) ? fmaxf(t, kTinyY) : __builtin_inff();
       if (__builtin_amdgcn_ballot_w64(!(ymin > thr)) == 0) return 0;
     }
     uint32_t m = 0;
@@ -606,14 +657,15 @@ __device__ __forceinline__ uint32_t lanes_max(const V *__restrict__ p, size_t co
   return m;
 }
 
-// maxC * kNegligible for the chunk's C rows [first, first + count) (element
-// offsets, whole rows), the same in every lane: the magnitudes, as bit
-// patterns, reduced over the wave's active lanes and then wave-wide with an
-// unsigned max. Rows of whole 16-byte vectors (C is 16-byte aligned) are read
-// as vectors, bf16 rows of even length as pairs. A NaN or infinity gives +inf.
+// The largest |C| over the chunk's C rows [first, first + count) (element
+// offsets, whole rows) as an fp32 bit pattern (0x7f800000 or more: a NaN or
+// an infinity), the same in every lane: the magnitudes, as bit patterns,
+// reduced over the wave's active lanes and then wave-wide with an unsigned
+// max. Rows of whole 16-byte vectors (C is 16-byte aligned) are read as
+// vectors, bf16 rows of even length as pairs.
 template <typename T, int NT>
-__device__ __forceinline__ float chunk_cscale(const T *__restrict__ C, size_t first,
-                                              size_t count) {
+__device__ __forceinline__ uint32_t chunk_cmax_bits(const T *__restrict__ C, size_t first,
+                                                    size_t count) {
   auto mag32 = [](uint32_t x) -> uint32_t {  // a 32-bit word: one fp32 or two bf16
     if constexpr (sizeof(T) == 2)
       return max((x << 16) & 0x7fffffffu, x & 0x7fff0000u);
@@ -634,11 +686,14 @@ __device__ __forceinline__ float chunk_cscale(const T *__restrict__ C, size_t fi
   } else {
     m = lanes_max(reinterpret_cast<const uint32_t *>(C + first), count, mag32);
   }
-  m = __ockl_wfred_max_u32(m);
+  return __ockl_wfred_max_u32(m);
+}
+// maxC * kNegligible from those bits (+inf for a non-finite C).
+__device__ __forceinline__ float cscale_of(uint32_t m) {
   return m >= 0x7f800000u ? __builtin_inff() : __uint_as_float(m) * kNegligible;
 }
 
-template <typename T, int NT, bool Gated>
+template <typename T, int NT, bool Gated, bool Careful>
 __device__ __forceinline__ float fix_step(float S, const Row<T, NT> &Cr, const float (&Ap)[NT],
                                           const float (&cin)[NT], uint32_t live) {
   float acc0 = 0.0f, acc1 = 0.0f;
@@ -649,7 +704,7 @@ __device__ __forceinline__ float fix_step(float S, const Row<T, NT> &Cr, const f
     for (int i = 0; i < kFixGroup; ++i) {
       const int n = g * kFixGroup + i;
       if (n < NT) {
-        const float v = cin[n] * exp2_hw(Ap[n] * S);
+        const float v = cin[n] * (Careful ? exp2_nz(Ap[n] * S) : exp2_hw(Ap[n] * S));
         if (n & 1)
           acc1 = __builtin_fmaf(Cr.get(n), v, acc1);
         else
@@ -672,7 +727,7 @@ constexpr int kFixWindow = 8;
 // the same sum the sequential sweep would. With ymirror, y changes are also
 // recorded in the other direction's words (min |y| of the new values), which
 // that direction's later fix reads. A tail of fewer than kPrefetch steps is
-// always evaluated in full. cscale is chunk_cscale of the chunk's C rows, or
+// always evaluated in full. cscale is cscale_of the chunk's largest |C|, or
 // +inf to leave the negligible-block test out.
 template <typename T, int NT, bool Reverse, class DX>
 __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *__restrict__ C,
@@ -694,6 +749,12 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   const size_t ss = size_t(g.d_inner);  // stride between blocks of the statistics
   const bool mirror = ymirror && len % kPrefetch == 0;
   const FixGroups<NT> groups(Ap, cin);
+  // A non-finite carry: its terms go through exp2_nz, so that an infinite
+  // carry times an exponential that flushed to zero stays infinite (rare).
+  bool nonfinite = false;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) nonfinite = nonfinite || !__builtin_isfinite(cin[n]);
+  const bool careful = __builtin_amdgcn_ballot_w64(nonfinite) != 0;
   // Loads what block k needs into (dr, yr, s_in): its delta and y words and
   // the running sum before it.
   // The loads also bring the block's C rows toward L2 (touched, held until
@@ -713,6 +774,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   auto run_block = [&](int k, const float (&dr)[kPrefetch], const float (&yr)[kPrefetch],
                        float S, uint32_t live, uint32_t touched) {
     keep_alive(touched);
+    const float S_in = S;  // the running sum before the block
     float Sj[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
@@ -720,18 +782,36 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
       Sj[j] = S;
     }
     const int i0 = k * kPrefetch;
-    Row<T, NT> Cc;
-    Cc.load(C + (row0 + tof(i0)) * NT);
     float ymin = 0.0f;
+    if (__builtin_expect(careful, false)) {
+      // Rare (a non-finite carry): step by step with exp2_nz, reading delta
+      // and y again, in a compact loop (a second unrolled copy of the block
+      // spilled registers in the common path).
+      float Sr = S_in;  // the same additions as Sj, so the same sums
+#pragma unroll 1
+      for (int j = 0; j < kPrefetch; ++j) {
+        const size_t r = row(i0 + j);
+        Sr += dx(ldv(&at(delta + r, io)));
+        Row<T, NT> Cc;
+        Cc.load(C + (row0 + tof(i0 + j)) * NT);
+        float &yref = at(y + r, yo);
+        const float yv = yref + fix_step<T, NT, true, true>(Sr, Cc, Ap, cin, live);
+        yref = yv;
+        ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
+      }
+    } else {
+      Row<T, NT> Cc;
+      Cc.load(C + (row0 + tof(i0)) * NT);
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
-      Row<T, NT> Cn;
-      wait_scalar_loads();
-      if (j + 1 < kPrefetch) Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
-      const float yv = yr[j] + fix_step<T, NT, true>(Sj[j], Cc, Ap, cin, live);
-      at(y + row(i0 + j), yo) = yv;
-      ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
-      if (j + 1 < kPrefetch) Cc = Cn;
+      for (int j = 0; j < kPrefetch; ++j) {
+        Row<T, NT> Cn;
+        wait_scalar_loads();
+        if (j + 1 < kPrefetch) Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
+        const float yv = yr[j] + fix_step<T, NT, true, false>(Sj[j], Cc, Ap, cin, live);
+        at(y + row(i0 + j), yo) = yv;
+        ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
+        if (j + 1 < kPrefetch) Cc = Cn;
+      }
     }
     if (mirror)
       reinterpret_cast<uint16_t *>(ymirror + s0 + size_t(nfull - 1 - k) * ss)[0] =
@@ -789,15 +869,58 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
     Row<T, NT> Cc;
     Cc.load(C + (row0 + tof(i)) * NT);
     float &yr = at(y + r, yo);
-    yr = yr + fix_step<T, NT, false>(S, Cc, Ap, cin, 0);
+    yr = yr + fix_step<T, NT, false, true>(S, Cc, Ap, cin, 0);
   }
+}
+
+// A chunk whose C rows hold an inf or NaN: y = sum_n C*(local state + carry
+// term) cannot be had as the chunk pass's sum_n C*(local state) plus a
+// correction sum_n C*(carry term) when C is infinite (inf*x + inf*z where the
+// recurrence forms inf*(x + z)). Such a chunk is evaluated again from its
+// exact incoming states, step by step, in each direction the call computes
+// (y overwritten: the forward sweep writes its output with D*u, the reverse
+// sweep adds its own), with exp2_nz. Only inputs with a non-finite C take
+// this path.
+template <typename T, int NT, class DX>
+__device__ void recompute_chunk(const T *__restrict__ u, const T *__restrict__ delta,
+                                const T *__restrict__ B, const T *__restrict__ C,
+                                const float (&Ap)[NT], float Dd, const DX &dx,
+                                const float *__restrict__ carry_f,
+                                const float *__restrict__ carry_r, float *__restrict__ y,
+                                const Geometry &g, int b, int c, int d, int t0, int t1,
+                                int direction) {
+  const size_t row0 = size_t(b) * g.L;
+  const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));
+  const uint32_t yo = uint32_t(d) * 4u;
+  auto run = [&](auto reverse, const float *carry, bool has_carry, bool accumulate) {
+    constexpr bool kRev = decltype(reverse)::value;
+    float h[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) h[n] = has_carry ? carry[agg_index(g, NT, b, c, n, d)] : 0.0f;
+#pragma unroll 1
+    for (int i = 0; i < t1 - t0; ++i) {
+      const int t = kRev ? t1 - 1 - i : t0 + i;
+      const size_t r = (row0 + t) * size_t(g.d_inner);
+      Row<T, NT> Bc, Cc;
+      Bc.load(B + (row0 + t) * NT);
+      Cc.load(C + (row0 + t) * NT);
+      const float out = s6_step<T, NT, true>(dx(ldv(&at(delta + r, io))), ldv(&at(u + r, io)),
+                                             Bc, Cc, Ap, Dd, h);
+      float &yr = at(y + r, yo);
+      yr = accumulate ? yr + out : out;
+    }
+  };
+  if (direction != SSM_DIR_REV)
+    run(std::false_type{}, carry_f, c > 0, false);
+  if (direction != SSM_DIR_FWD)
+    run(std::true_type{}, carry_r, c < g.nchunks - 1, direction == SSM_DIR_BIDIR);
 }
 
 template <typename T, int NT, class DX>
 __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
-    const T *__restrict__ delta, const float *__restrict__ dbias, const float *__restrict__ A,
-    const T *__restrict__ C,
-    float *__restrict__ y, const float *__restrict__ carry_f,
+    const T *__restrict__ u, const T *__restrict__ delta, const float *__restrict__ dbias,
+    const float *__restrict__ A, const T *__restrict__ B, const T *__restrict__ C,
+    const float *__restrict__ D, float *__restrict__ y, const float *__restrict__ carry_f,
     const float *__restrict__ carry_r, const float *__restrict__ sf_end,
     const uint32_t *__restrict__ sf_word, const float *__restrict__ sr_end,
     uint32_t *__restrict__ sr_word, Geometry g, int direction) {
@@ -813,12 +936,17 @@ __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
 #pragma unroll
   for (int n = 0; n < NT; ++n) Ap[n] = A[size_t(d) * NT + n] * kLog2e;
   const DX dx = make_dx<DX>(dbias, d);
+  const uint32_t cmax =
+      chunk_cmax_bits<T, NT>(C, (size_t(b) * g.L + t0) * NT, size_t(t1 - t0) * NT);
+  if (__builtin_expect(cmax >= 0x7f800000u, 0)) {  // wave-uniform: C holds an inf or NaN
+    recompute_chunk<T, NT, DX>(u, delta, B, C, Ap, D[d], dx, carry_f, carry_r, y, g, b, c, d,
+                               t0, t1, direction);
+    return;
+  }
   // Short chunks end before their carry has decayed far enough: no
   // negligible-block test.
   const float cscale =
-      (t1 - t0 >= kNegligibleMinLen && !g.full_fix)
-          ? chunk_cscale<T, NT>(C, (size_t(b) * g.L + t0) * NT, size_t(t1 - t0) * NT)
-          : __builtin_inff();
+      (t1 - t0 >= kNegligibleMinLen && !g.full_fix) ? cscale_of(cmax) : __builtin_inff();
   if (do_f) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) cin[n] = carry_f[agg_index(g, NT, b, c, n, d)];
@@ -926,8 +1054,8 @@ int launch_all(const S6Args &a, hipStream_t stream) {
                      agg_s, agg_f, agg_r, a.A, car_f, car_r, g, NT, a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 carry launch")) return rc;
   hipLaunchKernelGGL((s6_fix_kernel<T, NT, DX>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
-                     dl, a.delta_bias, a.A, C, a.y, car_f, car_r, sf_end, sf_word, sr_end,
-                     sr_word, g, a.direction);
+                     u, dl, a.delta_bias, a.A, B, C, a.D, a.y, car_f, car_r, sf_end, sf_word,
+                     sr_end, sr_word, g, a.direction);
   return hip_check(hipGetLastError(), "s6 fix launch");
 }
 

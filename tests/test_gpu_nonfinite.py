@@ -139,3 +139,57 @@ def test_nonfinite_batched_all_sequences(shape):
     assert_same_nonfinite(h, ref, TOL, f"batched {nseq}x{length}")
     assert_same_nonfinite(last, ref[:, -1], TOL, "h_last")
     assert np.array_equal(last, h[:, -1], equal_nan=True)  # the same values, bit for bit
+
+
+# ---- S6: non-finite inputs through the chunk, carry and fix passes ---------
+
+import oracle  # noqa: E402
+from mamba_s6_selective_amd.workloads import s6_inputs  # noqa: E402
+
+S6_CASES = {
+    # name -> list of (tensor, index, value); indices are (b, t, d) or (b, t, n)
+    "u+inf": [("u", (0, 700, 5), INF)],
+    "u-inf": [("u", (1, 1500, 9), -INF)],
+    "unan": [("u", (0, 300, 3), NAN)],
+    "u+inf then u-inf": [("u", (0, 700, 5), INF), ("u", (0, 1900, 5), -INF)],
+    # a huge delta: that step's exponential flushes in fp32 (the float64 value
+    # is tiny, not zero) right after an infinite state
+    "u+inf then huge delta": [("u", (0, 850, 7), INF), ("delta", (0, 900, 7), 200.0)],
+    "delta+inf": [("delta", (1, 1234, 2), INF)],
+    "B+inf": [("B", (0, 1000, 0), INF)],
+    "C+inf": [("C", (1, 2000, 0), -INF)],
+    "C=0 on an infinite state": [("u", (0, 700, 5), INF), ("C", (0, 1200, 0), 0.0)],
+}
+
+
+def s6_planted(case, N, seed=31):
+    inp = s6_inputs(2, 3000, 64, N, seed=seed, dtype="f32")
+    if N == 1:  # the first-order recurrence per channel: a = exp(delta A), b = delta u
+        inp.B = torch.ones_like(inp.B)
+        inp.C = torch.ones_like(inp.C)
+        inp.D = torch.zeros_like(inp.D)
+    for name, idx, v in S6_CASES[case]:
+        getattr(inp, name)[idx] = v
+    return inp
+
+
+@pytest.mark.parametrize("chunk", ["256", None])
+@pytest.mark.parametrize("N", [1, 16])
+@pytest.mark.parametrize("case", sorted(S6_CASES))
+def test_nonfinite_s6(case, N, chunk, monkeypatch):
+    """Every output against the float64 oracle, NaN and +-inf positions and
+    signs included, forward, reverse and bidirectional, with chunks of 256
+    steps (carries cross 11 chunk boundaries) and with the planner's."""
+    say(f"nonfinite s6 {case} N={N} chunk={chunk}")
+    if chunk:
+        monkeypatch.setenv("SSMSCAN_S6_CHUNK", chunk)
+    else:
+        monkeypatch.delenv("SSMSCAN_S6_CHUNK", raising=False)
+    dev = need_gpu()
+    inp = s6_planted(case, N)
+    t = [x.to(dev) for x in (inp.u, inp.delta, inp.A, inp.B, inp.C, inp.D)]
+    for direction in ("fwd", "rev", "bidir"):
+        y = ssm.selective_scan_fwd(*t, direction=direction).cpu().numpy()
+        with np.errstate(all="ignore"):
+            ref = oracle.selective_scan(*inp.as_f64(), direction=direction)
+        assert_same_nonfinite(y, ref, TOL, f"s6 {case} N={N} {direction}")
