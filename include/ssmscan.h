@@ -103,6 +103,22 @@ SSM_API int ssm_linear_scan(const float *a, const float *b, float h0, float *h, 
                             void *stream);
 
 /*
+ * ssm_linear_scan for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same recurrence, arguments, result bits and errors as ssm_linear_scan, but
+ * the look-back status words live in a fixed device array inside the
+ * library (about 4.3 MB per GPU, held until the process ends; its address is
+ * looked up once per device), so a call allocates nothing, frees nothing and
+ * sets no memory: it only enqueues the scan kernel. The array holds every
+ * size ssm_linear_scan accepts (n <= 2^31; larger n returns
+ * SSM_ERR_UNSUPPORTED). Every call on a GPU shares that GPU's array, on any
+ * stream: calls whose kernels overlap in time on one GPU race and can leave
+ * a later call waiting forever, so order them (one stream, or events).
+ */
+SSM_API int ssm_linear_scan_noalloc(const float *a, const float *b, float h0, float *h,
+                                    int64_t n, void *stream);
+
+/*
  * Batched form: nseq independent sequences of `len` elements each, stored one
  * after another (a, b, h are float[nseq][len]), for per-sequence carry-in and
  * carry-out -- e.g. the cross-chunk carries of a chunked scan, or a long

@@ -27,6 +27,7 @@ SSM_ERR_ALLOC = -4
 _P = ctypes.c_void_p
 SIGNATURES = {
     "ssm_linear_scan": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
+    "ssm_linear_scan_noalloc": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
     "ssm_linear_scan_3pass": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
     "ssm_linear_scan_hs": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, ctypes.c_int64, _P]),
     "ssm_linear_scan_batched": (ctypes.c_int, [_P] * 5 + [ctypes.c_int64, ctypes.c_int64, _P]),
@@ -196,6 +197,18 @@ def linear_scan(a, b, h0: float = 0.0, out=None):
     with torch.cuda.device(a.device):
         _check(lib.ssm_linear_scan(a.data_ptr(), b.data_ptr(), float(h0), out.data_ptr(),
                                    a.numel(), _stream(a)))
+    return out
+
+
+def linear_scan_noalloc(a, b, h0: float = 0.0, out=None):
+    """linear_scan through the library's allocation-free entry point (status
+    memory inside the library; calls on one GPU must not overlap)."""
+    import torch
+    lib = load_library()
+    out = _linear_args(a, b, out)
+    with torch.cuda.device(a.device):
+        _check(lib.ssm_linear_scan_noalloc(a.data_ptr(), b.data_ptr(), float(h0),
+                                           out.data_ptr(), a.numel(), _stream(a)))
     return out
 
 

@@ -66,6 +66,13 @@ hipError_t launch_linear_scan(const float *a, const float *b, float h0, float *h
 // Workgroups of the scan kernel that fit on one CU at once (0 on error).
 int linear_wgs_per_cu();
 
+// Status words of the allocation-free linear scan for the current device (a
+// file-scope device array of linear_noalloc_bytes() bytes holding up to
+// kLinearMaxTiles tiles; its address is looked up once per device). Returns 1
+// on success, 0 if the device or symbol lookup failed.
+int linear_noalloc_status(LinearStatus *status, uint32_t epoch_cycle);
+size_t linear_noalloc_bytes();
+
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n,
                            hipStream_t stream);
 

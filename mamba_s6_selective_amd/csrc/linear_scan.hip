@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -866,7 +867,49 @@ __global__ __launch_bounds__(256) void copy_kernel(const float *__restrict__ src
     dst[i] = src[i];
 }
 
+// Status memory of the allocation-free entry point: file-scope device memory,
+// one copy per GPU, sized for the largest launch (kLinearMaxTiles tiles,
+// 2^31 elements) in the workspace layout (claims word and done count, then
+// the three levels, each 256-byte aligned). It starts zeroed when the code
+// object is loaded: epoch 0 everywhere and the claims word at epoch 1 with
+// nothing claimed, which is the state every launch leaves for the next, so
+// it is never cleared again. In host code its name is not a device address:
+// linear_noalloc_status takes the address from hipGetSymbolAddress.
+constexpr size_t pad256(size_t x) { return (x + 255) / 256 * 256; }
+constexpr size_t kNoAllocLvl0 = pad256(size_t(kLinearMaxTiles) * sizeof(AggWord));
+constexpr size_t kNoAllocLvl1 = pad256(size_t(kLinearMaxTiles / 64) * sizeof(AggWord));
+constexpr size_t kNoAllocLvl2 = pad256(size_t(kLinearMaxTiles / 4096) * sizeof(AggWord));
+constexpr size_t kNoAllocBytes = 256 + kNoAllocLvl0 + kNoAllocLvl1 + kNoAllocLvl2;
+__device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
 }  // namespace
+
+size_t linear_noalloc_bytes() { return kNoAllocBytes; }
+
+int linear_noalloc_status(LinearStatus *status, uint32_t epoch_cycle) {
+  constexpr int kMaxDevices = 64;
+  static void *ptrs[kMaxDevices];  // per device: scratch's address there
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+      void *p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return 0;
+      ptrs[dev] = p;
+    }
+  }
+  char *base = static_cast<char *>(ptrs[dev]);
+  status->claims = reinterpret_cast<unsigned long long *>(base);
+  status->lvl0 = reinterpret_cast<AggWord *>(base + 256);
+  status->lvl1 = reinterpret_cast<AggWord *>(base + 256 + kNoAllocLvl0);
+  status->lvl2 = reinterpret_cast<AggWord *>(base + 256 + kNoAllocLvl0 + kNoAllocLvl1);
+  status->nwords = int64_t((kNoAllocBytes - 256) / sizeof(uint64_t));
+  status->epoch_cycle = epoch_cycle;
+  return 1;
+}
 
 int64_t linear_tile_elems(bool segmented) {
   return segmented ? Shape<true>::kTileElems : Shape<false>::kTileElems;

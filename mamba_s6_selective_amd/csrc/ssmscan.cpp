@@ -253,6 +253,53 @@ int ssm_linear_scan(const float *a, const float *b, float h0, float *h, int64_t 
                    "linear_scan launch");
 }
 
+int ssm_linear_scan_noalloc(const float *a, const float *b, float h0, float *h, int64_t n,
+                            void *stream) {
+  g_last_error.clear();
+  if (n < 0) return fail(SSM_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return SSM_OK;
+  if (!a || !b || !h) return fail(SSM_ERR_INVALID_ARG, "null pointer with n > 0");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(h))
+    return fail(SSM_ERR_INVALID_ARG, "a, b and h must be 16-byte aligned");
+  const int64_t tile = linear_tile_elems(false);
+  const int64_t ntiles = (n + tile - 1) / tile;
+  if (ntiles > kLinearMaxTiles)
+    return fail(SSM_ERR_UNSUPPORTED,
+                "n too large for the allocation-free scan (its status memory holds 2^31 elements)");
+  const size_t bytes = size_t(n) * sizeof(float);
+  if (overlap(h, bytes, a, bytes) || overlap(h, bytes, b, bytes))
+    return fail(SSM_ERR_INVALID_ARG, "h overlaps a or b");
+  // Resident workgroups per device, kept in a fixed table (nothing allocated).
+  constexpr int kMaxDevices = 64;
+  static int grids[kMaxDevices];
+  static std::mutex grid_mu;
+  int dev = 0;
+  if (int rc = current_device(&dev)) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(SSM_ERR_UNSUPPORTED, "device index too large");
+  int grid = 0;
+  {
+    std::lock_guard<std::mutex> lock(grid_mu);
+    if (grids[dev] == 0) {
+      int cus = 0;
+      if (int rc = hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                                                   dev), "hipDeviceGetAttribute"))
+        return rc;
+      int per_cu = linear_wgs_per_cu();
+      if (per_cu <= 0) return fail(SSM_ERR_HIP, "occupancy query for the scan kernel failed");
+      grids[dev] = cus * per_cu;
+    }
+    grid = grids[dev];
+  }
+  // The status memory's epochs always use the default cycle: it lives as
+  // long as the process, so its cycle cannot change under it.
+  LinearStatus status{};
+  if (!linear_noalloc_status(&status, kDefaultEpochCycle))
+    return fail(SSM_ERR_HIP, "looking up the allocation-free scan's status memory failed");
+  return hip_check(launch_linear_scan(a, b, h0, h, n, ntiles, status, grid, nullptr, nullptr, 0,
+                                      static_cast<hipStream_t>(stream)),
+                   "linear_scan_noalloc launch");
+}
+
 int ssm_linear_scan_batched(const float *a, const float *b, const float *h0, float *h,
                             float *h_last, int64_t nseq, int64_t len, void *stream) {
   g_last_error.clear();
