@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
@@ -75,6 +76,20 @@ def load_s6_traffic(name):
     return d.get("bytes_per_launch")
 
 
+def load_s6_valu(name):
+    """rocprofv3 VALUBusy (per cent of GPU time the VALUs issue) and VALU
+    instructions per (b, t, d, n) of each S6 pass on workload `name`, from a
+    committed counter summary, or None if absent or taken on a different
+    kernel source."""
+    f = PROFILES / "s6_valu.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text()).get(name)
+    if not d or d.get("kernel_source_sha") != source_hash("s6_scan.hip", "s6_internal.h"):
+        return None
+    return d.get("kernels")
+
+
 def time_steps(fn, steps, warmup):
     """Runs fn() warmup times (and on, untimed, until SETTLE["s"] seconds have
     passed, so that the clocks have settled), then `steps` timed times
@@ -124,6 +139,31 @@ def bench_linear(dev, steps, warmup):
     h = torch.empty_like(a)
     ms_step, ms_kernel = time_steps(lambda: ssm.linear_scan(a, b, 0.0, out=h), steps, warmup)
     return n, ms_step, ms_kernel
+
+
+def bench_linear_small(dev, steps, warmup):
+    """The n = 65,536 workload (a ~ U(0.9, 1)): its 786 KB stay in L2, so one
+    call is bound by launch and look-back latency, not by HBM. Reported as the
+    latency of one call (host clock around a call and a synchronisation,
+    median of 200) and as elements/s of calls issued back to back."""
+    import torch
+    import mamba_s6_selective_amd as ssm
+    from mamba_s6_selective_amd.workloads import LINEAR_WORKLOADS, linear_workload_inputs
+    name = "linear-n65536"
+    n = LINEAR_WORKLOADS[name]["n"]
+    a, b = linear_workload_inputs(name)
+    a, b = a.to(dev), b.to(dev)
+    h = torch.empty_like(a)
+    _, ms_kernel = time_steps(lambda: ssm.linear_scan(a, b, 0.0, out=h), steps * 10, warmup)
+    lat = []
+    for _ in range(200):
+        t0 = time.perf_counter()
+        ssm.linear_scan(a, b, 0.0, out=h)
+        torch.cuda.synchronize()
+        lat.append(time.perf_counter() - t0)
+    return {"workload": name, "n": n, "latency_us": round(statistics.median(lat) * 1e6, 2),
+            "ms_per_launch_back_to_back": round(ms_kernel, 5),
+            "elements_per_s": n / (ms_kernel * 1e-3)}
 
 
 def bench_linear_3pass(dev, steps, warmup, ms_single):
@@ -210,8 +250,9 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
     w = S6_WORKLOADS[name]
     inp = s6_workload_inputs(name)
     E, nbytes, tdn, other = s6_algorithmic(w)
-    # Rotate input sets so the working set exceeds the 256 MB Infinity Cache.
-    sets = max(1, min(8, int(1.0e9 // max(nbytes, 1)) + 1))
+    # Rotate input sets so the working set (over 512 MB) exceeds the 256 MB
+    # Infinity Cache.
+    sets = max(2, min(16, math.ceil(6.0e8 / max(nbytes, 1))))
     bufs = []
     for _ in range(sets):
         bufs.append([x.to(dev).clone() for x in (inp.u, inp.delta, inp.A, inp.B, inp.C, inp.D)]
@@ -224,10 +265,12 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
         ssm.selective_scan_fwd(*t[:6], direction=w["direction"], out=t[6])
 
     ms_step, ms_kernel = time_steps(step, steps, warmup)
+    extra = {}
     fused = None
     if w["direction"] == "fwd" and w["dtype"] == "bf16":
         # the same scan with delta given before its activation and softplus fused in
         pre = [inp.delta_pre.to(dev).clone() for _ in range(sets)]
+        dl = [torch.empty_like(p) for p in pre]
 
         def step_fused():
             t = bufs[k[0] % sets]
@@ -235,10 +278,57 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
                                    out=t[6], delta_softplus=True)
             k[0] += 1
 
+        def step_softplus():  # the separate elementwise pass the fusion saves
+            j = k[0] % sets
+            torch.nn.functional.softplus(pre[j], out=dl[j])
+            k[0] += 1
+
+        def step_separate():  # that pass, then the scan on its output
+            j = k[0] % sets
+            t = bufs[j]
+            torch.nn.functional.softplus(pre[j], out=dl[j])
+            ssm.selective_scan_fwd(t[0], dl[j], *t[2:6], direction=w["direction"], out=t[6])
+            k[0] += 1
+
         _, ms_fused = time_steps(step_fused, steps, warmup)
+        _, ms_sp = time_steps(step_softplus, steps, warmup)
+        _, ms_sep = time_steps(step_separate, steps, warmup)
         fused = {"ms_kernel_avg": round(ms_fused, 4),
                  "ratio_to_unfused": round(ms_fused / ms_kernel, 3),
-                 "separate_pass_bytes": 2 * E * (2 if w["dtype"] == "bf16" else 4)}
+                 "separate_pass_bytes": 2 * E * (2 if w["dtype"] == "bf16" else 4),
+                 "separate_softplus_ms": round(ms_sp, 4),
+                 "separate_softplus_then_scan_ms": round(ms_sep, 4),
+                 "ratio_to_separate": round(ms_fused / ms_sep, 3)}
+        # The fix pass skips carry terms that are exactly zero and blocks whose
+        # correction rounds away, so its cost depends on how fast the states
+        # decay: with every term evaluated, and with A 64 times closer to 0.
+        os.environ["SSMSCAN_S6_FULL_FIX"] = "1"
+        try:
+            _, ms_full = time_steps(step, steps, warmup)
+        finally:
+            del os.environ["SSMSCAN_S6_FULL_FIX"]
+        for t in bufs:
+            t[2].div_(64.0)  # A[d, n] = -(n + 1) / 64
+        try:
+            _, ms_slow = time_steps(step, steps, warmup)
+        finally:
+            for t in bufs:
+                t[2].mul_(64.0)
+        extra["general_A"] = {
+            "full_fix_ms": round(ms_full, 4), "ratio_full_fix": round(ms_full / ms_kernel, 3),
+            "slow_decay_A": "-(n+1)/64", "slow_decay_ms": round(ms_slow, 4),
+            "ratio_slow_decay": round(ms_slow / ms_kernel, 3)}
+    if w["direction"] == "bidir":
+        # the fused call against one forward and one reverse call on the same inputs
+        def step_separate_dirs():
+            t = bufs[k[0] % sets]
+            ssm.selective_scan_fwd(*t[:6], direction="fwd", out=t[6])
+            ssm.selective_scan_fwd(*t[:6], direction="rev", out=t[6])
+            k[0] += 1
+
+        _, ms_two = time_steps(step_separate_dirs, steps, warmup)
+        extra["fusion"] = {"separate_fwd_plus_rev_ms": round(ms_two, 4),
+                           "fusion_ratio": round(ms_two / ms_kernel, 3)}
     lane_cycles = tdn * (other + exp_cost)
     alu_frac = lane_cycles / (ms_kernel * 1e-3) / (VALU_PEAK_T * 1e12)
     gbs = nbytes / (ms_kernel * 1e-3) / 1e9
@@ -251,7 +341,9 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
                      "traffic": load_s6_traffic(name)},
         "hbm": {"achieved_GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4),
                 "algorithmic_bytes": nbytes},
+        "valu_rocprof": load_s6_valu(name),
         "fused_softplus": fused,
+        **extra,
     }
 
 
@@ -276,6 +368,25 @@ def cpu_baseline(budget_s):
     return {"value": n / med, "unit": "elements/s", "cores": 1, "kind": "oracle",
             "sample": f"whole n=2^27 sequence, float64 C loop, {len(times)} passes "
                       f"(median {med:.3f} s)"}
+
+
+def cpu_baseline_small():
+    """The float64 C oracle on the whole n = 65,536 workload, single thread."""
+    import numpy as np
+    from mamba_s6_selective_amd.workloads import linear_workload_inputs
+    from oracle import native
+    a, b = linear_workload_inputs("linear-n65536")
+    a = a.numpy().astype(np.float64)
+    b = b.numpy().astype(np.float64)
+    native.load()
+    times = []
+    for _ in range(50):
+        t0 = time.perf_counter()
+        native.linear_scan(a, b, 0.0)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": a.size / med, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole n=65536 sequence, float64 C loop, 50 passes (median {med * 1e6:.0f} us)"}
 
 
 def cpu_baseline_batched(budget_s, nseq=4096, length=32768):
@@ -391,6 +502,8 @@ def main():
                      "traffic": traffic},
         "copy_kernel_GBs": round(copy_gbs, 1),
     }
+    record["linear_n65536"] = bench_linear_small(dev, args.steps, args.warmup)
+    log(f"linear n=65536: {record['linear_n65536']['latency_us']} us per synchronised call")
     record["three_pass"] = bench_linear_3pass(dev, max(5, args.steps // 2), 2, ms_kernel)
     log(f"three-pass: {record['three_pass']['ms_per_launch'] * 1e3:.1f} us, ratio "
         f"{record['three_pass']['measured_ratio']} (model {record['three_pass']['predicted_ratio']})")
@@ -407,6 +520,7 @@ def main():
         record["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
         # the three-pass scan computes the same workload: the same oracle run
         record["three_pass"]["cpu_baseline"] = record["cpu_baseline"]
+        record["linear_n65536"]["cpu_baseline"] = cpu_baseline_small()
         record["batched"]["cpu_baseline"] = cpu_baseline_batched(args.cpu_seconds / 4)
         for r in record.get("s6", []):
             r["cpu_baseline"] = cpu_baseline_s6(r["workload"], args.cpu_seconds / 4)

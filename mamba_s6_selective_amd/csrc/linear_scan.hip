@@ -107,19 +107,34 @@ __device__ __forceinline__ bool word_ready(uint64_t w, uint32_t epoch) {
 }
 
 // Composition, in lane order, of the maps held by lanes [0, count) of the
-// wave (later lanes contribute the identity). Fixed DPP tree: the result
-// depends only on the values and `count`. Returned in every lane. Op is a
-// careful rule; when every word of the window is finite and no head, the
-// plain rule gives the same values except that a total multiplier that
-// underflowed must be nudged (unless a word's multiplier is exactly zero),
-// which is what the common case does.
-// The careful case is rare; it runs as a loop of cross-lane shuffles (one
-// copy of the code, not one per window: unrolled DPP steps at every window
-// doubled the control wave's code and slowed the scan through instruction
-// fetch). Still a fixed shape, so the result depends only on the words.
+// wave (later lanes contribute the identity), returned in every lane. A fixed
+// shape: the result depends only on the values and `count`.
+//  window_total: plain products in one DPP tree;
+//  window_total_careful: Op's rule (mul_nz products, heads honoured). With
+//    all values finite that is the plain tree, with the head bits or-ed and a
+//    multiplier that underflowed to zero nudged (unless a lane holds an exact
+//    zero; a head's multiplier is exactly zero, so plain products already
+//    drop what precedes it). Otherwise a loop of cross-lane shuffles, one
+//    copy of the code (unrolled DPP steps at every window doubled the control
+//    wave's code and slowed the scan through instruction fetch).
+__device__ __forceinline__ Map window_total(Map m, int count, int lane) {
+  if (lane >= count) m = identity_map();
+  wave_scan<AffOp<false, false>>(m);
+  return lane_map(m, 63);
+}
 template <class Op>
-__device__ __forceinline__ Map window_total_careful(Map m) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ Map window_total_careful(Map m, int count, int lane) {
+  if (lane >= count) m = identity_map();
+  const bool odd = !__builtin_isfinite(m.a) || !__builtin_isfinite(m.b);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(odd) == 0, 1)) {
+    const bool zero = __builtin_amdgcn_ballot_w64(m.a == 0.0f) != 0;
+    const uint32_t head = __builtin_amdgcn_ballot_w64(m.head != 0u) != 0 ? 1u : 0u;
+    wave_scan<AffOp<false, false>>(m);
+    Map t = lane_map(m, 63);
+    if (t.a == 0.0f && !zero) t.a = nudge(t.a);
+    t.head = head;
+    return t;
+  }
 #pragma unroll 1
   for (int d = 1; d < 64; d *= 2) {
     Map p;
@@ -130,29 +145,13 @@ __device__ __forceinline__ Map window_total_careful(Map m) {
   }
   return lane_map(m, 63);
 }
-// Seg: heads are common (the batched form), so the plain rule honours them;
-// otherwise a head (a tile evaluated in sequence) is rare and takes the
-// careful path with the non-finite words.
-template <class Op, bool Seg>
-__device__ __forceinline__ Map window_total(Map m, int count, int lane) {
-  if (lane >= count) m = identity_map();
-  const bool odd =
-      !__builtin_isfinite(m.a) || !__builtin_isfinite(m.b) || (!Seg && m.head != 0u);
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(odd) != 0, 0))  // uniform; rare
-    return window_total_careful<Op>(m);
-  const bool zero = __builtin_amdgcn_ballot_w64(m.a == 0.0f) != 0;
-  wave_scan<AffOp<Seg, false>>(m);
-  Map t = lane_map(m, 63);
-  if (t.a == 0.0f && !zero) t.a = nudge(t.a);
-  return t;
-}
 
 // Look-back windows at level 0: the tile's own superblock and the
 // kRecent - 1 superblocks before it. Older superblocks are read at level 1 and
 // older blocks at level 2, but the words of those recent superblocks (and of
 // the block they may straddle into) come from look-backs that may still be
 // running when this one starts, so they are composed here from level-0 words.
-constexpr int kRecent = 5;
+constexpr int kRecent = 6;
 
 // Resumable look-back of one tile: which words it reads, the words read so
 // far and, per lane, whether that lane's word is complete. The tile's prefix
@@ -164,14 +163,6 @@ struct LookBack {
   int nw, n0, n1, n2;
   uint64_t wa[kRecent], wb[kRecent], w1a, w1b, w2a, w2b;
   bool r[kRecent], r1, r2;
-};
-
-// Prefixes of one tile: P0 over the earlier tiles of its superblock, PB over
-// everything from the start of block blk1 up to its superblock, and h_in
-// (h0 pushed through the level-2 prefix, then PB, then P0).
-struct Prefix {
-  Map p0, pb;
-  float h_in;
 };
 
 __device__ __forceinline__ void lb_init(LookBack &s, int64_t tile, int lane) {
@@ -224,51 +215,128 @@ __device__ __forceinline__ void lb_check(LookBack &s, uint32_t epoch) {
   s.r2 = s.r2 || (word_ready(s.w2a, epoch) && word_ready(s.w2b, epoch));
 }
 
-__device__ __forceinline__ bool lb_done(const LookBack &s) {
-  bool pending = __ballot(!s.r1) != 0 || __ballot(!s.r2) != 0;
+// Words lb_done waits for: all of them, or only those a tile that closes a
+// superblock (block: also closes a block) needs for the aggregates it
+// publishes (see publish_higher).
+enum class Need { kAll, kSuperblock, kBlock };
+
+__device__ __forceinline__ bool lb_done(const LookBack &s, Need need = Need::kAll) {
+  bool pending = false;
+  if (need == Need::kAll) pending = __ballot(!s.r2) != 0;
+  if (need != Need::kSuperblock) pending = pending || __ballot(!s.r1) != 0;
 #pragma unroll
-  for (int q = 0; q < kRecent; ++q) pending = pending || __ballot(!s.r[q]) != 0;
+  for (int q = 0; q < kRecent; ++q)
+    if (need != Need::kSuperblock || q == s.nw - 1) pending = pending || __ballot(!s.r[q]) != 0;
   return !pending;
 }
 
-// Composition of the complete look-back windows (fixed shapes: the result
-// depends only on the words and the tile index). Op is a careful rule: the
-// published aggregates' multipliers are usually underflowed products.
-template <class Op, bool Seg>
-__device__ Prefix lb_finish(const LookBack &s, float h0, int lane) {
-  const Map p2 = window_total<Op, Seg>(word_map(s.w2a, s.w2b), s.n2, lane);
-  Map pb = window_total<Op, Seg>(word_map(s.w1a, s.w1b), s.n1, lane);
-  Prefix pf;
-  pf.p0 = identity_map();
-#pragma unroll
-  for (int q = 0; q < kRecent; ++q) {
-    if (q < s.nw - 1) {  // a whole earlier superblock
-      pb = Op::compose(pb, window_total<Op, Seg>(word_map(s.wa[q], s.wb[q]), kFan, lane));
-    } else if (q == s.nw - 1) {  // the tile's own superblock, up to the tile
-      pf.p0 = window_total<Op, Seg>(word_map(s.wa[q], s.wb[q]), s.n0, lane);
-    }
-  }
-  pf.pb = pb;
-  const float h2 = Op::apply(p2, h0);
-  const float h1 = Op::apply(pb, h2);
-  pf.h_in = Op::apply(pf.p0, h1);
-  return pf;
+// Entries of recent window q.
+__device__ __forceinline__ int window_count(const LookBack &s, int q) {
+  return q < s.nw - 1 ? kFan : (q == s.nw - 1 ? s.n0 : 0);
 }
 
-// Once a tile's own aggregate is known: the last tile of a superblock
-// publishes the superblock's aggregate (level 1), and the last tile of a
-// block the block's aggregate (level 2). For the last tile of a block, blk1
-// is its own block, so PB (+) P0 (+) own covers the whole block.
+// Window q of the look-back in sequence order, q = -2 (level 2), -1 (level
+// 1), 0 .. kRecent - 1 (recent level-0 windows), as this lane's map and the
+// window's entry count; selected, not indexed, so the words stay in
+// registers. For the rolled loops of the rare careful paths.
+__device__ __forceinline__ Map window_word(const LookBack &s, int q, int &count) {
+  uint64_t wa = s.w2a, wb = s.w2b;
+  count = s.n2;
+  if (q == -1) {
+    wa = s.w1a;
+    wb = s.w1b;
+    count = s.n1;
+  }
+#pragma unroll
+  for (int k = 0; k < kRecent; ++k) {
+    if (q == k) {
+      wa = s.wa[k];
+      wb = s.wb[k];
+      count = window_count(s, k);
+    }
+  }
+  return word_map(wa, wb);
+}
+
+// The tile's incoming value: h0 pushed through the complete windows in
+// sequence order (level 2, level 1, then the recent level-0 windows; fixed
+// shapes, so the result depends only on the words and the tile index).
+// Plain products, which agree with the careful rule whenever h0 and every
+// word are finite: a head's multiplier is exactly zero, so a plain product
+// also drops what precedes it, and a multiplier that underflowed to zero
+// instead of to the smallest subnormal changes a finite value by at most
+// 2^-149 of the value it multiplies.
+__device__ __forceinline__ float lb_value(const LookBack &s, float h0, int lane) {
+  using P = AffOp<false, false>;
+  float v = P::apply(window_total(word_map(s.w2a, s.w2b), s.n2, lane), h0);
+  v = P::apply(window_total(word_map(s.w1a, s.w1b), s.n1, lane), v);
+#pragma unroll
+  for (int q = 0; q < kRecent; ++q) {
+    const int count = window_count(s, q);
+    if (count > 0) v = P::apply(window_total(word_map(s.wa[q], s.wb[q]), count, lane), v);
+  }
+  return v;
+}
+
+// The same by Op's rule (window totals by window_total_careful, heads
+// honoured), one window at a time.
+template <class Op>
+__device__ __forceinline__ float lb_value_careful(const LookBack &s, float h0, int lane) {
+  float v = h0;
+#pragma unroll 1
+  for (int q = -2; q < kRecent; ++q) {
+    int count;
+    const Map m = window_word(s, q, count);
+    if (count > 0) v = Op::apply(window_total_careful<Op>(m, count, lane), v);
+  }
+  return v;
+}
+
+// Plain, or careful when the plain value is an inf or NaN: a non-finite h0 or
+// word always leaves it so (no IEEE step of a plain window total or of
+// applying it to a value turns a non-finite value finite again), and the
+// careful rule can differ only then.
+template <class Op>
+__device__ __forceinline__ float lb_finish(const LookBack &s, float h0, int lane) {
+  const float v = lb_value(s, h0, lane);
+  if (__builtin_expect(!uniform_nonfinite(v), 1)) return v;
+  return lb_value_careful<Op>(s, h0, lane);
+}
+
+// The last tile of a superblock publishes the superblock's aggregate (level
+// 1): its own superblock's level-0 window composed with its own aggregate.
+// The last tile of a block also publishes the block's aggregate (level 2):
+// the level-1 window of its block and its recent level-0 windows before its
+// superblock, composed with the superblock's aggregate. Neither needs any
+// word from before the block, so both are published before the tile's
+// level-2 words arrive; every aggregate is thus a fixed-depth function of
+// level-0 words and no chain of look-backs runs through the higher levels.
+// Careful rule throughout: a later look-back may push an inf through these
+// multipliers.
 template <class Op>
 __device__ __forceinline__ void publish_higher(const LinearStatus &st, int64_t tile,
-                                               const Prefix &pf, const Map &own, uint32_t epoch,
-                                               int lane) {
+                                               const LookBack &s, const Map &own,
+                                               uint32_t epoch, int lane) {
   const int64_t sb = tile / kFan;
   const int64_t blk = sb / kFan;
-  if (tile - sb * kFan != kFan - 1 || lane != 0) return;
-  const Map sbm = Op::compose(pf.p0, own);
-  st_map(st.lvl1[sb], epoch, sbm);
-  if (sb - blk * kFan == kFan - 1) st_map(st.lvl2[blk], epoch, Op::compose(pf.pb, sbm));
+  const bool closes_block = sb - blk * kFan == kFan - 1;
+  // Windows -1 .. nw - 2 (the block's level-1 window and the whole recent
+  // superblocks) go into PB, which only the last tile of a block needs;
+  // window nw - 1 (the own superblock up to the tile) is P0.
+  Map pb = identity_map(), sbm = own;
+#pragma unroll 1
+  for (int q = closes_block ? -1 : s.nw - 1; q < s.nw; ++q) {
+    int count;
+    const Map t = window_total_careful<Op>(window_word(s, q, count), count, lane);
+    if (q == s.nw - 1)
+      sbm = Op::compose(t, own);
+    else
+      pb = Op::compose(pb, t);
+  }
+  if (lane == 0) {
+    st_map(st.lvl1[sb], epoch, sbm);
+    if (closes_block) st_map(st.lvl2[blk], epoch, Op::compose(pb, sbm));
+  }
 }
 
 // Independent sequences inside one scan (the batched form): `len` elements
@@ -764,26 +832,43 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
     auto step = [&](LookBack &lp, LookBack &ln) {
       const int64_t tn = sh.ids[j & 3];  // claimed before barrier C of iteration j-3
       if (tp < ntiles) {
-        lb_check(lp, epoch);
-        while (!lb_done(lp)) {
-          __builtin_amdgcn_s_sleep(1);
-          lb_issue(lp, st, lane);
-          lb_check(lp, epoch);
-        }
         const int rp = (j - 1) & 3;
-        const Prefix pf = lb_finish<HOp, Seg>(lp, h0, lane);
-        if (__builtin_expect(sh.tile_seq[rp] != 0, 0)) {  // rare: an inf or NaN in the tile
-          const Map own{0.0f, seq_tile<Seg>(sh, (j - 1) & 1, tp, pf.h_in, h, n, sg), 1u};
-          if (lane == 0) st_map(st.lvl0[tp], epoch, own);
-          publish_higher<HOp>(st, tp, pf, own, epoch, lane);
-        } else {
-          publish_higher<HOp>(st, tp, pf, sh.tile[rp], epoch, lane);
-          if (lane == 0) {
-            float c = pf.h_in;
-            for (int w = 0; w < kWaves; ++w) {
-              sh.carry[rp][w] = c;
-              c = COp::apply(sh.wave[rp][w], c);
+        const bool seq = sh.tile_seq[rp] != 0;  // rare: an inf or NaN in the tile
+        const int64_t sb = tp / kFan;
+        // A tile that closes a superblock publishes as soon as the words its
+        // aggregates need are complete (before the rest, unless it is
+        // evaluated in sequence: then its own aggregate is its final value).
+        // One call site each for lb_finish and publish_higher.
+        bool publish = tp - sb * kFan == kFan - 1;
+        Need need = Need::kAll;
+        if (publish && !seq)
+          need = (sb & (kFan - 1)) == kFan - 1 ? Need::kBlock : Need::kSuperblock;
+        Map own = sh.tile[rp];
+        float h_in = 0.0f;
+        lb_check(lp, epoch);
+        for (;;) {
+          while (!lb_done(lp, need)) {
+            __builtin_amdgcn_s_sleep(1);
+            lb_issue(lp, st, lane);
+            lb_check(lp, epoch);
+          }
+          if (need == Need::kAll) {
+            h_in = lb_finish<HOp>(lp, h0, lane);
+            if (__builtin_expect(seq, 0)) {
+              own = Map{0.0f, seq_tile<Seg>(sh, (j - 1) & 1, tp, h_in, h, n, sg), 1u};
+              if (lane == 0) st_map(st.lvl0[tp], epoch, own);
             }
+          }
+          if (publish) publish_higher<HOp>(st, tp, lp, own, epoch, lane);
+          publish = false;
+          if (need == Need::kAll) break;
+          need = Need::kAll;
+        }
+        if (!seq && lane == 0) {
+          float c = h_in;
+          for (int w = 0; w < kWaves; ++w) {
+            sh.carry[rp][w] = c;
+            c = COp::apply(sh.wave[rp][w], c);
           }
         }
       }

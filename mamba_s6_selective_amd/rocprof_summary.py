@@ -16,6 +16,15 @@
         (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled by
         the ratio of the bytes the copy kernel moves (copy_bytes read,
         copy_bytes written) to what the same counter reads for it.
+        With --key NAME the record is merged into the --out file under NAME.
+
+    python -m mamba_s6_selective_amd.rocprof_summary valu VALU_results.db \\
+        --kernel s6_chunk_kernel s6_carry_kernel s6_fix_kernel --tdn 1073741824 \\
+        --source s6_scan.hip s6_internal.h --out profiles/s6_valu.json --key NAME
+        Per kernel (median over dispatches): VALUBusy, and VALU and
+        transcendental instructions per (b, t, d, n) element (wave
+        instructions x 64 lanes / tdn), from a run that collected VALUBusy,
+        SQ_INSTS_VALU, SQ_INSTS_VALU_TRANS_F32 and SQ_WAVES.
 """
 from __future__ import annotations
 
@@ -112,10 +121,35 @@ def cmd_traffic(args):
         "bytes_per_launch": kf * 1024.0 * f_scale + kw * 1024.0 * w_scale,
         "kernel_source_sha": source_sha(*args.source),
     }
+    write_record(rec, args.out, args.key)
+
+
+def write_record(rec, out, key):
+    """Print rec; write it to out, or merge it into out under key."""
     text = json.dumps(rec, indent=1)
-    if args.out:
-        Path(args.out).write_text(text + "\n")
+    if out and key:
+        f = Path(out)
+        d = json.loads(f.read_text()) if f.exists() else {}
+        d[key] = rec
+        f.write_text(json.dumps(d, indent=1) + "\n")
+    elif out:
+        Path(out).write_text(text + "\n")
     print(text)
+
+
+def cmd_valu(args):
+    per = {c: counter_per_dispatch(args.db, c)
+           for c in ("VALUBusy", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES")}
+    kernels = {}
+    for k in args.kernel:
+        def med(c):
+            return statistics.median(pick(per[c], k))
+        kernels[k] = {"VALUBusy_pct": round(med("VALUBusy"), 2),
+                      "valu_per_tdn": round(med("SQ_INSTS_VALU") * 64 / args.tdn, 4),
+                      "trans_per_tdn": round(med("SQ_INSTS_VALU_TRANS_F32") * 64 / args.tdn, 4),
+                      "waves": med("SQ_WAVES")}
+    rec = {"kernels": kernels, "tdn": args.tdn, "kernel_source_sha": source_sha(*args.source)}
+    write_record(rec, args.out, args.key)
 
 
 def main(argv=None):
@@ -135,8 +169,18 @@ def main(argv=None):
     t.add_argument("--source", required=True, nargs="+",
                    help="csrc files the kernel is built from (hashed in this order)")
     t.add_argument("--out")
+    t.add_argument("--key")
+    v = sub.add_parser("valu")
+    v.add_argument("db")
+    v.add_argument("--kernel", required=True, nargs="+", help="kernel names (substrings)")
+    v.add_argument("--tdn", type=float, required=True,
+                   help="(b, t, d, n) elements of one call (lane instructions are divided by it)")
+    v.add_argument("--source", required=True, nargs="+")
+    v.add_argument("--out")
+    v.add_argument("--key")
     args = ap.parse_args(argv)
-    {"stats": cmd_stats, "counters": cmd_counters, "traffic": cmd_traffic}[args.cmd](args)
+    {"stats": cmd_stats, "counters": cmd_counters, "traffic": cmd_traffic,
+     "valu": cmd_valu}[args.cmd](args)
 
 
 if __name__ == "__main__":
