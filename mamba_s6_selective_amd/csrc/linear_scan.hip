@@ -387,13 +387,14 @@ __device__ __forceinline__ uint32_t seg_heads(int64_t i, int64_t n, const Segmen
 
 // Loads one tile (rows of float4 per wave); past n the identity map (1, 0).
 // With segments, the first element of every sequence has its b replaced by
-// a*h0 + b (its value, whatever precedes it) and its head bit set in hd.
+// a*h0 + b (its value, whatever precedes it) and its multiplier set to zero;
+// hd is non-zero if the lane holds a head.
 template <bool Seg>
 __device__ __forceinline__ void load_tile(const float *__restrict__ a,
                                           const float *__restrict__ b, int64_t n, int64_t tile,
                                           const Segments &sg, float4 (&va)[Shape<Seg>::kRows],
                                           float4 (&vb)[Shape<Seg>::kRows],
-                                          uint32_t (&hd)[Shape<Seg>::kRows]) {
+                                          uint32_t &hd) {
   constexpr int kRows = Shape<Seg>::kRows, kWaveElems = Shape<Seg>::kWaveElems,
                 kTileElems = Shape<Seg>::kTileElems;
   const int lane = threadIdx.x & 63;
@@ -421,19 +422,19 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ a,
       vb[r] = make_float4(tb[0], tb[1], tb[2], tb[3]);
     }
   }
-#pragma unroll
-  for (int r = 0; r < kRows; ++r) hd[r] = 0u;
+  hd = 0u;
   if constexpr (Seg) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const int64_t off = wave_start + r * kRowElems + lane * 4;
-      hd[r] = seg_heads(off, n, sg);
-      if (hd[r]) {
+      const uint32_t bits = seg_heads(off, n, sg);
+      hd |= bits;
+      if (bits) {
         float ta[4] = {va[r].x, va[r].y, va[r].z, va[r].w};
         float tb[4] = {vb[r].x, vb[r].y, vb[r].z, vb[r].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if ((hd[r] >> j) & 1u) {
+          if ((bits >> j) & 1u) {
             uint32_t k, t;
             seg_pos(uint32_t(off + j), sg, k, t);
             tb[j] = __builtin_fmaf(ta[j], sg.h0 ? sg.h0[k] : 0.0f, tb[j]);
@@ -447,10 +448,6 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ a,
   }
 }
 
-__device__ __forceinline__ Map item_map(float a, float b, uint32_t hd, int j) {
-  return Map{a, b, (hd >> j) & 1u};
-}
-
 // Data waves, phase 1: the lane's 4 items composed, a wave scan per row (im:
 // the lane's inclusive prefix within its row) and the wave's aggregate (rows
 // folded in order), returned in every lane. Plain products; a multiplier
@@ -461,21 +458,25 @@ __device__ __forceinline__ Map item_map(float a, float b, uint32_t hd, int j) {
 // and an offset may have met an underflowed zero, and an infinite multiplier
 // is no affine map at all): the tile is then evaluated in sequence instead
 // (seq_tile) and these results are not used.
+// Sequence heads (batched scans) need no rule of their own here: a head's
+// multiplier is exactly zero, so with finite values a plain product already
+// drops what precedes it. Only the wave aggregate carries a head bit (set if
+// the wave holds a head), for the careful compositions downstream, and
+// tile_apply honours heads itself when the incoming value is not finite.
 template <bool Seg, int kRows>
 __device__ __forceinline__ bool tile_local_scan(const float4 (&va)[kRows],
                                                 const float4 (&vb)[kRows],
-                                                const uint32_t (&hd)[kRows], Map (&im)[kRows],
-                                                Map &wagg) {
-  using Op = AffOp<Seg, false>;
-  using COp = AffOp<Seg, true>;
+                                                uint32_t hd, Map (&im)[kRows], Map &wagg) {
+  using Op = AffOp<false, false>;
+  using COp = AffOp<false, true>;
   const int lane = threadIdx.x & 63;
   bool bad = false;
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
-    Map m = item_map(va[r].x, vb[r].x, hd[r], 0);
-    m = Op::compose(m, item_map(va[r].y, vb[r].y, hd[r], 1));
-    m = Op::compose(m, item_map(va[r].z, vb[r].z, hd[r], 2));
-    m = Op::compose(m, item_map(va[r].w, vb[r].w, hd[r], 3));
+    Map m = Map{va[r].x, vb[r].x, 0u};
+    m = Op::compose(m, Map{va[r].y, vb[r].y, 0u});
+    m = Op::compose(m, Map{va[r].z, vb[r].z, 0u});
+    m = Op::compose(m, Map{va[r].w, vb[r].w, 0u});
     wave_scan<Op>(m);
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(m.a == 0.0f) != 0, 0)) {  // an underflow or a zero
       const float z = fminf(fminf(fabsf(va[r].x), fabsf(va[r].y)),
@@ -484,16 +485,10 @@ __device__ __forceinline__ bool tile_local_scan(const float4 (&va)[kRows],
       const uint64_t upto = ~uint64_t(0) >> (63 - lane);  // lanes 0 .. lane
       if (m.a == 0.0f && (zeros & upto) == 0) m.a = nudge(m.a);
     }
-    if constexpr (Seg) {
-      // A head inside the row discards what precedes it from the row's total,
-      // so every lane's prefix is looked at.
-      const bool nf = !__builtin_isfinite(m.a) || !__builtin_isfinite(m.b);
-      bad = bad || __builtin_amdgcn_ballot_w64(nf) != 0;
-    }
     im[r] = m;
   }
-  // Without heads an inf or NaN anywhere in a row leaves the row's total
-  // non-finite (no IEEE operation of a composition turns it finite again).
+  // An inf or NaN anywhere in a row leaves the row's total non-finite (no
+  // IEEE operation of a plain composition turns it finite again).
   wagg = lane_map(im[0], 63);
   bad = bad || uniform_nonfinite(wagg.a) || uniform_nonfinite(wagg.b);
 #pragma unroll
@@ -502,6 +497,7 @@ __device__ __forceinline__ bool tile_local_scan(const float4 (&va)[kRows],
     bad = bad || uniform_nonfinite(t.a) || uniform_nonfinite(t.b);
     wagg = COp::compose(wagg, t);
   }
+  if constexpr (Seg) wagg.head = __builtin_amdgcn_ballot_w64(hd != 0u) != 0 ? 1u : 0u;
   return bad;
 }
 
@@ -513,7 +509,6 @@ __device__ __forceinline__ void tile_apply(const float4 (&va)[kRows], const floa
                                            const Map (&im)[kRows], float c,
                                            float *__restrict__ h, int64_t n, int64_t tile,
                                            const Segments &sg) {
-  using Op = AffOp<Seg, true>;
   constexpr int kWaveElems = Shape<Seg>::kWaveElems, kTileElems = Shape<Seg>::kTileElems;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -521,22 +516,36 @@ __device__ __forceinline__ void tile_apply(const float4 (&va)[kRows], const floa
   const bool full = (tile + 1) * kTileElems <= n;
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
-    const float end = Op::apply(im[r], c);                  // h after this lane's chunk
-    const float cin = dpp<kWaveShr1, 0xf, 0xf>(c, end);     // h before it
     const int64_t off = wave_start + r * kRowElems + lane * 4;
+    // A head's multiplier is exactly zero, so while the values are finite
+    // the plain recurrence already ignores what precedes a head.
+    const float end = __builtin_fmaf(im[r].a, c, im[r].b);  // h after this lane's chunk
+    const float cin = dpp<kWaveShr1, 0xf, 0xf>(c, end);     // h before it
     float4 o;
     o.x = __builtin_fmaf(va[r].x, cin, vb[r].x);
     o.y = __builtin_fmaf(va[r].y, o.x, vb[r].y);
     o.z = __builtin_fmaf(va[r].z, o.y, vb[r].z);
     o.w = __builtin_fmaf(va[r].w, o.z, vb[r].w);
     if constexpr (Seg) {
-      const uint32_t hb = seg_heads(off, n, sg);
-      if (hb) {  // a head ignores the value before it
-        o.x = (hb & 1u) ? vb[r].x : o.x;
+      // An inf or NaN carry (from an earlier sequence: the tile's own values
+      // are finite) must not reach past a head: a lane whose prefix holds a
+      // head takes the prefix's offset, and a head item takes its own.
+      if (__builtin_expect(uniform_nonfinite(c), 0)) {
+        const uint32_t hb = seg_heads(off, n, sg);
+        const uint64_t heads = __builtin_amdgcn_ballot_w64(hb != 0u);
+        const uint64_t upto = ~uint64_t(0) >> (63 - lane);
+        const float e = (heads & upto) ? im[r].b : end;
+        const float ci = dpp<kWaveShr1, 0xf, 0xf>(c, e);
+        o.x = (hb & 1u) ? vb[r].x : __builtin_fmaf(va[r].x, ci, vb[r].x);
         o.y = (hb & 2u) ? vb[r].y : __builtin_fmaf(va[r].y, o.x, vb[r].y);
         o.z = (hb & 4u) ? vb[r].z : __builtin_fmaf(va[r].z, o.y, vb[r].z);
         o.w = (hb & 8u) ? vb[r].w : __builtin_fmaf(va[r].w, o.z, vb[r].w);
+        c = lane_f(e, 63);
+      } else {
+        c = lane_f(end, 63);
       }
+    } else {
+      c = lane_f(end, 63);
     }
     if (full) {
       store_nt(h + off, o);
@@ -559,7 +568,6 @@ __device__ __forceinline__ void tile_apply(const float4 (&va)[kRows], const floa
         }
       }
     }
-    c = lane_f(end, 63);
   }
 }
 
@@ -627,6 +635,7 @@ struct Shared {
   static constexpr int kWaves = Shape<Seg>::kWaves, kRows = Shape<Seg>::kRows;
   float4 park[2][kWaves][kRows][2][64];  // a, b rows of two parked tiles
   Map wave[4][kWaves];                   // per-wave aggregates
+  float2 wpre[4][kWaves];                // their inclusive prefixes (plain products)
   Map tile[4];                           // tile aggregates
   uint32_t wave_seq[4][kWaves];          // the wave's rows hold an inf or NaN
   uint32_t tile_seq[4];                  // so does the tile: evaluated in sequence (seq_tile)
@@ -712,11 +721,10 @@ __device__ __forceinline__ float seq_tile(const Shared<Seg> &sh, int slot, int64
 template <bool Seg, int kRows = Shape<Seg>::kRows>
 __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
                                                  const float4 (&vb)[kRows],
-                                                 const uint32_t (&hd)[kRows], Map (&im)[kRows],
+                                                 uint32_t hd, Map (&im)[kRows],
                                                  Shared<Seg> &sh, int ring, int slot,
                                                  const LinearStatus &st, int64_t tile,
                                                  uint32_t epoch) {
-  using COp = AffOp<Seg, true>;
   constexpr int kWaves = Shape<Seg>::kWaves;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -732,19 +740,32 @@ __device__ __forceinline__ void scan_and_publish(const float4 (&va)[kRows],
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
   prior = __builtin_amdgcn_readfirstlane(prior);
   if (prior == kWaves - 1) {
-    Map g = sh.wave[ring][0];
-    uint32_t seq = sh.wave_seq[ring][0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      g = COp::compose(g, sh.wave[ring][w]);
-      seq |= sh.wave_seq[ring][w];
+    // The fold is on the path to the tile's publication: one LDS round trip
+    // (lane w reads wave w's aggregate) and a DPP scan. Plain products give
+    // the careful rule's map when every wave aggregate is finite (the only
+    // case in which it is published): a head's multiplier is exactly zero,
+    // and an underflow is nudged at the end unless a wave's multiplier is
+    // exactly zero. The inclusive prefixes go to LDS for the carries.
+    Map x = identity_map();
+    uint32_t sq = 0u;
+    if (lane < kWaves) {
+      x = sh.wave[ring][lane];
+      sq = sh.wave_seq[ring][lane];
     }
+    const bool zero = __builtin_amdgcn_ballot_w64(x.a == 0.0f) != 0;
+    const uint32_t head = __builtin_amdgcn_ballot_w64(x.head != 0u) != 0 ? 1u : 0u;
+    const uint32_t tseq = __builtin_amdgcn_ballot_w64(sq != 0u) != 0 ? 1u : 0u;
+    wave_scan<AffOp<false, false>>(x);
+    if (lane < kWaves) sh.wpre[ring][lane] = make_float2(x.a, x.b);
+    Map g = lane_map(x, kWaves - 1);
+    if (g.a == 0.0f && !zero) g.a = nudge(g.a);
+    g.head = head;
     if (lane == 0) {
       // A tile evaluated in sequence is published by the control wave once
       // it has its value (see seq_tile).
-      if (!seq) st_map(st.lvl0[tile], epoch, g);
+      if (!tseq) st_map(st.lvl0[tile], epoch, g);
       sh.tile[ring] = g;
-      sh.tile_seq[ring] = seq;
+      sh.tile_seq[ring] = tseq;
       sh.arrived[slot] = 0;  // reused two tiles later, after two barriers
     }
   }
@@ -834,6 +855,8 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
       if (tp < ntiles) {
         const int rp = (j - 1) & 3;
         const bool seq = sh.tile_seq[rp] != 0;  // rare: an inf or NaN in the tile
+        // Prefix of the waves before this lane's wave (read before the wait).
+        const float2 pre = lane > 0 && lane < kWaves ? sh.wpre[rp][lane - 1] : make_float2(1.0f, 0.0f);
         const int64_t sb = tp / kFan;
         // A tile that closes a superblock publishes as soon as the words its
         // aggregates need are complete (before the rest, unless it is
@@ -864,11 +887,19 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
           if (need == Need::kAll) break;
           need = Need::kAll;
         }
-        if (!seq && lane == 0) {
-          float c = h_in;
-          for (int w = 0; w < kWaves; ++w) {
-            sh.carry[rp][w] = c;
-            c = COp::apply(sh.wave[rp][w], c);
+        if (!seq) {
+          // The waves' aggregates are finite: with a finite h_in, the plain
+          // prefix of the waves before wave w applied to h_in gives the
+          // careful rule's value (a head's multiplier is exactly zero).
+          if (__builtin_expect(!uniform_nonfinite(h_in), 1)) {
+            if (lane < kWaves)
+              sh.carry[rp][lane] = lane == 0 ? h_in : __builtin_fmaf(pre.x, h_in, pre.y);
+          } else if (lane == 0) {
+            float c = h_in;
+            for (int w = 0; w < kWaves; ++w) {
+              sh.carry[rp][w] = c;
+              c = COp::apply(sh.wave[rp][w], c);
+            }
           }
         }
       }
@@ -896,7 +927,7 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
   // Register stages: (va, vb) tile being applied, (na, nb) tile being
   // scanned, (ma, mb) tile being loaded; prefixes of the two parked tiles.
   float4 va[kRows], vb[kRows], na[kRows], nb[kRows];
-  uint32_t hv[kRows], hn[kRows];
+  uint32_t hv, hn;
   Map imp[kRows], imw[kRows];
   if (t0 < ntiles) load_tile<Seg>(a, b, n, t0, sg, va, vb, hv);
   __syncthreads();  // A1
@@ -914,7 +945,7 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
     int64_t claimed = ntiles;
     if (wave == 0 && t2 < ntiles) claimed = successor(t2, ntiles, st, lane);
     float4 ma[kRows], mb[kRows];
-    uint32_t hm[kRows];
+    uint32_t hm;
     if (t2 < ntiles) load_tile<Seg>(a, b, n, t2, sg, ma, mb, hm);
     Map nim[kRows];
     if (t1 < ntiles)
@@ -932,8 +963,8 @@ __global__ __launch_bounds__(Shape<Seg>::kThreads + 64) void linear_scan_kernel(
       imw[r] = nim[r];
       na[r] = ma[r];
       nb[r] = mb[r];
-      hn[r] = hm[r];
     }
+    hn = hm;
     tp = t0;
     t0 = t1;
     t1 = t2;
