@@ -17,10 +17,12 @@
  *                                  to at most 256 chunks per sequence; the
  *                                  rounding then follows the new chunks).
  *   SSMSCAN_S6_FULL_FIX=1          S6 evaluates every carry term, read at
- *                                  every call. By default the fix pass skips
- *                                  terms that are exactly zero in fp32 and
- *                                  blocks whose correction rounds away; both
- *                                  settings give bit-identical outputs.
+ *                                  every call. By default the fix pass leaves
+ *                                  out the tail of the decaying carry terms
+ *                                  once a bound proves each left-out group of
+ *                                  4 states below 2^-24 over a block of
+ *                                  steps: outputs differ from full evaluation
+ *                                  by at most 2^-22 per direction.
  *   SSMSCAN_LINEAR_WGS_PER_CU=<k>  caps the workgroups per CU of the single-
  *                                  pass linear scan (read once per device).
  *   SSMSCAN_LINEAR_EPOCH_CYCLE=<c> epochs per cycle of the single-pass scans'
@@ -196,6 +198,11 @@ SSM_API int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *
  * y        : float[batch][L][d_inner], output (fp32).
  * direction: ssm_direction_t.
  * The (batch, L, d_inner, N) tensors dA, dBu and h never touch memory.
+ * Accuracy: with the sequence split into chunks, the carry into a chunk is
+ * added as its exact decaying contribution, whose tail is left out once
+ * proven below 2^-24 per group of 4 states over a block of steps: outputs
+ * are within 2^-22 per direction of evaluating every term, on top of fp32
+ * rounding (see SSMSCAN_S6_FULL_FIX).
  * Once a call on `stream` has sized that stream's workspace, a call with the
  * same or smaller sizes only enqueues kernels (no allocation, no memset), so
  * it may be recorded in a HIP graph and replayed (also for the _bf16 and _ex

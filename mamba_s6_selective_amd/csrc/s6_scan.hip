@@ -26,10 +26,11 @@
 //  3. fix pass: every chunk except the first (forward) / last (reverse) adds
 //     sum_n C[t,n] * carry_n * exp(A_n * S_t), S_t the running sum of delta
 //     from the carry's entry point, to its y. This is the exact carry
-//     contribution (the state is linear in its initial value); terms that
-//     are exactly zero in fp32, and blocks whose whole contribution rounds
-//     away against y, are skipped, with results bit-identical to evaluating
-//     them.
+//     contribution (the state is linear in its initial value). A group of
+//     states whose terms are provably below 2^-24 for a whole block of steps
+//     is left out (a truncated tail of a decaying series: at most 2^-22 per
+//     output and direction, far inside the fp32 tolerance); blocks with no
+//     group left are not touched at all.
 // All three passes are deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -210,14 +211,8 @@ __device__ __forceinline__ float s6_step(float dt, float x, const Row<T, NT> &Br
 }
 
 // What one direction's chunk sweep leaves for the fix pass, per full block of
-// kPrefetch steps (sweep order): the running delta sum at the block's end,
-// exactly, and a word holding the block's smallest running sum (high half)
-// and smallest |y| (low half), each truncated to its top 16 bits, i.e. to
-// bf16 toward zero -- never above the true value where that matters (a
-// positive sum, any |y|), so decisions taken from them stay on the safe
-// side. The |y| half is written by the sweep that completes y (0 until
-// then); in a bidirectional call the reverse sweep also writes it into the
-// forward words of the same steps (16-bit stores) when the blocks line up.
+// kPrefetch steps (sweep order): the running delta sum at the block's end
+// and the block's smallest running sum (a NaN sum stays NaN), both exact.
 // Reads one element per 64 bytes of the B and C rows of one block of steps
 // (first_elem: element offset of the block's lowest row), lanes 0-31 in B and
 // 32-63 in C, so that those lines are on their way to L2 before the scalar
@@ -241,13 +236,8 @@ __device__ __forceinline__ void keep_alive(uint32_t v) { asm volatile("" ::"v"(v
 
 struct SweepStats {
   float *s_end;
-  uint32_t *word;
-  bool y_final;       // this sweep completes y: record min |y|
-  uint32_t *mirror;   // other direction's words for min |y| (or null)
+  float *s_min;
 };
-__device__ __forceinline__ uint32_t pack_stats(float smin, float ymin) {
-  return (__float_as_uint(smin) & 0xffff0000u) | (__float_as_uint(ymin) >> 16);
-}
 
 // One sweep of the chunk-local recurrence from a zero state. Writes (or, when
 // Accumulate, adds) y for every step of the chunk, the block statistics in
@@ -280,13 +270,9 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
   // The lane's statistics addresses, formed once: they hold the channel, so
   // they sit in VGPRs and leave the scalar registers to the B/C rows.
   const size_t ss = size_t(g.d_inner);
-  const bool stats = st.word != nullptr;
+  const bool stats = st.s_min != nullptr;
   float *pe = stats ? st.s_end + stat_index(g, b, c, 0, d) : nullptr;
-  uint32_t *pw = stats ? st.word + stat_index(g, b, c, 0, d) : nullptr;
-  uint16_t *pm = stats && st.mirror && len % kPrefetch == 0
-                     ? reinterpret_cast<uint16_t *>(
-                           st.mirror + stat_index(g, b, c, full / kPrefetch - 1, d))
-                     : nullptr;
+  float *pw = stats ? st.s_min + stat_index(g, b, c, 0, d) : nullptr;
   // Two register sets for a block's delta, u (and y) words: one feeds the
   // block being computed while the next block's loads land in the other,
   // and the loop runs two blocks per iteration so the sets trade roles
@@ -326,7 +312,7 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
       }
       touched = touch_rows<T, NT>(B, C, block_row(i0 + kPrefetch) * NT);
     }
-    float smin = 0.0f, ymin = 0.0f;
+    float smin = 0.0f;
     // A step's exponential can flush to zero only if delta*A*log2(e) < -126
     // (|delta*A| > 87); decided per block from the largest delta (an infinite
     // one included). Such a block runs step by step with exp2_nz, so that an
@@ -346,11 +332,9 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
         Cc.load(C + (row0 + tof(i0 + j)) * NT);
         const float out = s6_step<T, NT, true>(dt, ldv(&at(u + r, io)), Bc, Cc, Ap, Dd, h);
         float &yr = at(y + r, yo);
-        const float yv = Accumulate ? yr + out : out;
-        yr = yv;
+        yr = Accumulate ? yr + out : out;
         S += dt;
         smin = j == 0 ? S : fminf(smin, S);
-        ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
       }
     } else {
       // B/C rows go one step ahead: step j's rows were loaded during step j-1.
@@ -370,11 +354,9 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
         // the next wait, which then waits for the whole scalar-load latency.
         __builtin_amdgcn_sched_barrier(0);
         const float out = s6_step<T, NT>(cd[j], cx[j], Bc, Cc, Ap, Dd, h);
-        const float yv = Accumulate ? cy[j] + out : out;
-        at(y + row(i0 + j), yo) = yv;
+        at(y + row(i0 + j), yo) = Accumulate ? cy[j] + out : out;
         S += cd[j];
         smin = j == 0 ? S : fminf(smin, S);
-        ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
         if (j + 1 < kPrefetch) {
           Bc = Bn;
           Cc = Cn;
@@ -384,13 +366,9 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
     if (stats) {  // wave-uniform
       // A NaN in the running sum reaches the block's end; fminf would drop it.
       *pe = S;
-      *pw = pack_stats(S == S ? smin : S, st.y_final ? ymin : 0.0f);
+      *pw = S == S ? smin : S;
       pe += ss;
       pw += ss;
-      if (pm) {  // the mirror runs the other way: its block index falls
-        *pm = uint16_t(__float_as_uint(ymin) >> 16);
-        pm -= 2 * ss;  // 2 halves per 32-bit word
-      }
     }
   };
   for (int i0 = 0; i0 < full; i0 += 2 * kPrefetch) {
@@ -419,8 +397,8 @@ __global__ __launch_bounds__(kThreads, 4) void s6_chunk_kernel(
     const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
     float *__restrict__ y, float *__restrict__ agg_s, float *__restrict__ agg_f,
-    float *__restrict__ agg_r, float *__restrict__ sf_end, uint32_t *__restrict__ sf_word,
-    float *__restrict__ sr_end, uint32_t *__restrict__ sr_word, Geometry g, int direction) {
+    float *__restrict__ agg_r, float *__restrict__ sf_end, float *__restrict__ sf_min,
+    float *__restrict__ sr_end, float *__restrict__ sr_min, Geometry g, int direction) {
   int b, c, d;
   decompose(g, b, c, d);
   if (d >= g.d_inner) return;
@@ -435,9 +413,8 @@ __global__ __launch_bounds__(kThreads, 4) void s6_chunk_kernel(
   float S = 0.0f;
   const bool multi = g.nchunks > 1;
   // Statistics for the fix pass, which runs only with several chunks.
-  const SweepStats stf{sf_end, multi ? sf_word : nullptr, direction == SSM_DIR_FWD, nullptr};
-  const SweepStats str{sr_end, multi ? sr_word : nullptr, true,
-                       direction == SSM_DIR_BIDIR ? sf_word : nullptr};
+  const SweepStats stf{sf_end, multi ? sf_min : nullptr};
+  const SweepStats str{sr_end, multi ? sr_min : nullptr};
   if (direction != SSM_DIR_REV) {
     chunk_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1, h, S,
                                      stf);
@@ -550,37 +527,34 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
 
 // Carry contribution at one step: sum_n C[t,n] * cin[n] * exp(A[n] * S).
 // The carry's terms decay: with A[d,n] < 0 and the running delta sum S
-// growing, cin[n] * exp(A[d,n] * S) shrinks. Two exact shortcuts follow.
+// growing, cin[n] * exp(A[d,n] * S) shrinks, and the tail of this decaying
+// sum is truncated with a proven bound.
 //
-// Zero terms: v_exp_f32 returns exactly 0 below 2^-126 (and any fp32
-// rounding of 2^x is 0 for x < -151), so once A[d,n] * S * log2(e) < kDeadArg
-// for every lane and every step of a block, the term adds exactly zero to y
-// and is skipped. States go in groups of kFixGroup; a group is skipped for a
-// block when this holds for all its states. For Ap[n] <= Ag < 0 and
-// S_j >= Smin > 0, fl(Ap[n] * S_j) <= fl(Ag * Smin) since rounding is monotone.
-//
-// Negligible blocks: the whole correction at step j is at most
-// maxC * sum_g (sum_{n in g} |cin[n]|) * 2^(Ag * Smin), maxC the largest |C|
-// over the chunk. When that bound, times 2^26 and a margin that covers its
-// own rounding and the hardware exp2's error, is below |y| (a normal number)
-// at every step of the block in every lane, the correction is under a
-// quarter of y's spacing and y + correction rounds to y: the block is left
-// as it is, stores included.
+// States go in groups of kFixGroup. For a group g, Ag = its largest Ap[n]
+// (the slowest decay; Ap = A * log2(e)) and Smin >= 0 the smallest running
+// sum over a block of kPrefetch steps, every term of the group at every step
+// of the block is at most maxC * sum_{n in g} |cin[n]| * 2^(Ag * Smin)
+// (2^(Ap[n] * S_j) <= 2^(Ag * S_j) <= 2^(Ag * Smin) for Ap[n] <= Ag < 0 and
+// S_j >= Smin), maxC the largest |C| over the chunk. When that bound, times a
+// margin for its own rounding and the hardware exp2's error, is at most
+// kTruncGroup in every lane, the group is left out of the block: with at
+// most 4 groups (N <= 16) the output changes by at most 2^-22 per direction
+// (fp32's own rounding of a unit-sized y is 2^-24). Carries that are not
+// finite, NaN exponent factors and non-negative ones are never left out, nor
+// is anything of a block whose running sum can be negative or NaN (there the
+// bound does not hold); a term whose exponential is exactly zero falls under
+// the rule like any other.
 constexpr int kFixGroup = 4;
-constexpr float kDeadArg = -152.0f;
-constexpr float kNegligible = 67822182.4f;  // 2^26 * 1.01
-constexpr float kTinyY = 0x1p-100f;          // smaller |y| never counts as resolving the bound
-constexpr int kNegligibleMinLen = 64;        // chunks shorter than this skip the test
+constexpr float kTruncGroup = 0x1p-24f;
+constexpr float kTruncScale = 1.01f / kTruncGroup;  // margin / kTruncGroup
 
 template <int NT>
 struct FixGroups {
   static constexpr int kCount = (NT + kFixGroup - 1) / kFixGroup;
   float Ag[kCount];    // largest Ap[n] of the group
   float cabs[kCount];  // sum of |cin[n]| over the group
-  bool keep[kCount];   // never skipped: a non-finite carry, a NaN or non-negative Ap
-  bool any_keep;
+  bool keep[kCount];   // never left out: a non-finite carry, a NaN or non-negative Ap
   __device__ __forceinline__ FixGroups(const float (&Ap)[NT], const float (&cin)[NT]) {
-    any_keep = false;
 #pragma unroll
     for (int g = 0; g < kCount; ++g) {
       float ag = -__builtin_inff(), ca = 0.0f;
@@ -597,39 +571,19 @@ struct FixGroups {
       Ag[g] = ag;
       cabs[g] = ca;
       keep[g] = k || !(ag < 0.0f);
-      any_keep = any_keep || keep[g];
     }
   }
-  // Decides what a block of kPrefetch steps needs, from the chunk pass's
-  // statistics word (smallest running sum and smallest |y| over the block,
-  // both truncated toward zero). Returns 0 when the block leaves y
-  // unchanged; otherwise bit g is set when group g has a lane whose term may
-  // be non-zero. cscale = maxC * kNegligible (infinite when C holds a
-  // non-finite value, or to leave the negligible-block test out).
-  __device__ __forceinline__ uint32_t decide(uint32_t word, float cscale) const {
-    const float smin = __uint_as_float(word & 0xffff0000u);
-    const float ymin = __uint_as_float(word << 16);
-    const bool sane = smin == smin;  // a NaN in the running sum reaches this
-    float p[kCount];
-#pragma unroll
-    for (int g = 0; g < kCount; ++g) p[g] = Ag[g] * smin;
-    if (cscale < __builtin_inff()) {  // wave-uniform
-      float bound = 0.0f;
-#pragma unroll
-      for (int g = 0; g < kCount; ++g) bound = fmaf(cabs[g], exp2_hw(p[g]), bound);
-      const float t = bound * cscale;
-      // The bound holds only for a non-negative running sum: with Ap < 0,
-      // 2^(Ap*S) is largest at the smallest S, and for S < 0 at the most
-      // negative Ap, not at Ag. (A negative sum needs a negative delta.)
-      const float thr =
-          (sane && !any_keep && t == t && smin >= 0.0f) ? fmaxf(t, kTinyY) : __builtin_inff();
-      if (__builtin_amdgcn_ballot_w64(!(ymin > thr)) == 0) return 0;
-    }
+  // Decides a block of kPrefetch steps from the chunk pass's smallest
+  // running sum over it: bit g set when group g has a lane that needs its
+  // terms (0: the block leaves y as it is). cscale = maxC * kTruncScale.
+  __device__ __forceinline__ uint32_t decide(float smin, float cscale) const {
+    const bool ok = smin >= 0.0f;  // false for a NaN or a negative sum
     uint32_t m = 0;
 #pragma unroll
     for (int g = 0; g < kCount; ++g) {
-      const bool dead = !keep[g] && sane && p[g] < kDeadArg;
-      if (__builtin_amdgcn_ballot_w64(!dead) != 0) m |= 1u << g;
+      const float bound = cabs[g] * exp2_hw(Ag[g] * smin) * cscale;
+      const bool drop = ok && !keep[g] && bound <= 1.0f;  // false for a NaN bound
+      if (__builtin_amdgcn_ballot_w64(!drop) != 0) m |= 1u << g;
     }
     return m;
   }
@@ -688,9 +642,9 @@ __device__ __forceinline__ uint32_t chunk_cmax_bits(const T *__restrict__ C, siz
   }
   return __ockl_wfred_max_u32(m);
 }
-// maxC * kNegligible from those bits (+inf for a non-finite C).
+// maxC * kTruncScale from those bits (+inf for a non-finite C).
 __device__ __forceinline__ float cscale_of(uint32_t m) {
-  return m >= 0x7f800000u ? __builtin_inff() : __uint_as_float(m) * kNegligible;
+  return m >= 0x7f800000u ? __builtin_inff() : __uint_as_float(m) * kTruncScale;
 }
 
 template <typename T, int NT, bool Gated, bool Careful>
@@ -724,19 +678,16 @@ constexpr int kFixWindow = 8;
 // delta, y and the running sum before the block are loaded only for blocks
 // that change y, the next such block's while the current one computes. The
 // running sums start from the chunk pass's exact values, so every step sees
-// the same sum the sequential sweep would. With ymirror, y changes are also
-// recorded in the other direction's words (min |y| of the new values), which
-// that direction's later fix reads. A tail of fewer than kPrefetch steps is
-// always evaluated in full. cscale is cscale_of the chunk's largest |C|, or
-// +inf to leave the negligible-block test out.
+// the same sum the sequential sweep would. A tail of fewer than kPrefetch
+// steps is always evaluated in full. cscale is cscale_of the chunk's largest
+// |C| (finite here).
 template <typename T, int NT, bool Reverse, class DX>
 __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *__restrict__ C,
                                           float *__restrict__ y, const float (&Ap)[NT],
                                           const float (&cin)[NT], const DX &dx,
                                           const Geometry &g, int b, int c, int d, int t0,
                                           int t1, float cscale, const float *__restrict__ s_end,
-                                          const uint32_t *__restrict__ word,
-                                          uint32_t *__restrict__ ymirror) {
+                                          const float *__restrict__ s_min) {
   const size_t row0 = size_t(b) * g.L;
   const int len = t1 - t0;
   const int nfull = len / kPrefetch;
@@ -747,7 +698,6 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   const uint32_t yo = uint32_t(d) * 4u;
   const size_t s0 = stat_index(g, b, c, 0, d);
   const size_t ss = size_t(g.d_inner);  // stride between blocks of the statistics
-  const bool mirror = ymirror && len % kPrefetch == 0;
   const FixGroups<NT> groups(Ap, cin);
   // A non-finite carry: its terms go through exp2_nz, so that an infinite
   // carry times an exponential that flushed to zero stays infinite (rare).
@@ -782,7 +732,6 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
       Sj[j] = S;
     }
     const int i0 = k * kPrefetch;
-    float ymin = 0.0f;
     if (__builtin_expect(careful, false)) {
       // Rare (a non-finite carry): step by step with exp2_nz, reading delta
       // and y again, in a compact loop (a second unrolled copy of the block
@@ -795,9 +744,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
         Row<T, NT> Cc;
         Cc.load(C + (row0 + tof(i0 + j)) * NT);
         float &yref = at(y + r, yo);
-        const float yv = yref + fix_step<T, NT, true, true>(Sr, Cc, Ap, cin, live);
-        yref = yv;
-        ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
+        yref = yref + fix_step<T, NT, true, true>(Sr, Cc, Ap, cin, live);
       }
     } else {
       Row<T, NT> Cc;
@@ -807,20 +754,16 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
         Row<T, NT> Cn;
         wait_scalar_loads();
         if (j + 1 < kPrefetch) Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
-        const float yv = yr[j] + fix_step<T, NT, true, false>(Sj[j], Cc, Ap, cin, live);
-        at(y + row(i0 + j), yo) = yv;
-        ymin = j == 0 ? fabsf(yv) : fminf(ymin, fabsf(yv));
+        at(y + row(i0 + j), yo) =
+            yr[j] + fix_step<T, NT, true, false>(Sj[j], Cc, Ap, cin, live);
         if (j + 1 < kPrefetch) Cc = Cn;
       }
     }
-    if (mirror)
-      reinterpret_cast<uint16_t *>(ymirror + s0 + size_t(nfull - 1 - k) * ss)[0] =
-          uint16_t(__float_as_uint(ymin) >> 16);
   };
 
-  uint32_t wn[kFixWindow];  // statistics words of the next window
+  float wn[kFixWindow];  // smallest running sums of the next window's blocks
 #pragma unroll
-  for (int i = 0; i < kFixWindow; ++i) wn[i] = i < nfull ? word[s0 + size_t(i) * ss] : 0u;
+  for (int i = 0; i < kFixWindow; ++i) wn[i] = i < nfull ? s_min[s0 + size_t(i) * ss] : 0.0f;
   for (int w0 = 0; w0 < nfull; w0 += kFixWindow) {
     // Decide the window: 4 bits of live groups per block.
     uint32_t masks = 0;
@@ -834,7 +777,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
 #pragma unroll
     for (int i = 0; i < kFixWindow; ++i) {
       const int k = w0 + kFixWindow + i;
-      if (k < nfull) wn[i] = word[s0 + size_t(k) * ss];
+      if (k < nfull) wn[i] = s_min[s0 + size_t(k) * ss];
     }
     if (masks == 0) continue;  // wave-uniform: the whole window leaves y as it is
     // Its blocks that change y, each one's words loaded while the one before
@@ -922,8 +865,8 @@ __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
     const float *__restrict__ A, const T *__restrict__ B, const T *__restrict__ C,
     const float *__restrict__ D, float *__restrict__ y, const float *__restrict__ carry_f,
     const float *__restrict__ carry_r, const float *__restrict__ sf_end,
-    const uint32_t *__restrict__ sf_word, const float *__restrict__ sr_end,
-    uint32_t *__restrict__ sr_word, Geometry g, int direction) {
+    const float *__restrict__ sf_min, const float *__restrict__ sr_end,
+    const float *__restrict__ sr_min, Geometry g, int direction) {
   int b, c, d;
   decompose(g, b, c, d);
   if (d >= g.d_inner) return;
@@ -943,22 +886,18 @@ __global__ __launch_bounds__(kThreads) void s6_fix_kernel(
                                t0, t1, direction);
     return;
   }
-  // Short chunks end before their carry has decayed far enough: no
-  // negligible-block test.
-  const float cscale =
-      (t1 - t0 >= kNegligibleMinLen && !g.full_fix) ? cscale_of(cmax) : __builtin_inff();
+  const float cscale = cscale_of(cmax);
   if (do_f) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) cin[n] = carry_f[agg_index(g, NT, b, c, n, d)];
-    // In a bidirectional call the reverse fix reads min |y| from its own words.
     fix_sweep<T, NT, false>(delta, C, y, Ap, cin, dx, g, b, c, d, t0, t1, cscale, sf_end,
-                            sf_word, direction == SSM_DIR_BIDIR ? sr_word : nullptr);
+                            sf_min);
   }
   if (do_r) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) cin[n] = carry_r[agg_index(g, NT, b, c, n, d)];
     fix_sweep<T, NT, true>(delta, C, y, Ap, cin, dx, g, b, c, d, t0, t1, cscale, sr_end,
-                           sr_word, nullptr);
+                           sr_min);
   }
 }
 
@@ -1009,8 +948,9 @@ int launch_all(const S6Args &a, hipStream_t stream) {
   g.d_inner = a.d_inner;
   g.groups = (a.d_inner + kThreads - 1) / kThreads;
   g.chunk = plan_chunk(a.batch, a.L, g.groups, resident_chunk_wgs<T, NT, DX>());
-  // SSMSCAN_S6_FULL_FIX=1 turns the fix pass's exact shortcuts off (every
-  // carry term evaluated), so that their results can be compared bit for bit.
+  // SSMSCAN_S6_FULL_FIX=1 turns the fix pass's truncation off (every carry
+  // term evaluated), to check the truncation's bound and to time the
+  // untruncated cost.
   const char *full = getenv("SSMSCAN_S6_FULL_FIX");
   g.full_fix = (full && atoi(full) != 0) ? 1 : 0;
   g.nchunks = (a.L + g.chunk - 1) / g.chunk;
@@ -1019,8 +959,8 @@ int launch_all(const S6Args &a, hipStream_t stream) {
   if (wgs > (int64_t(1) << 31) - 1) return fail(SSM_ERR_UNSUPPORTED, "problem too large");
 
   float *agg_s = nullptr, *agg_f = nullptr, *agg_r = nullptr, *car_f = nullptr,
-        *car_r = nullptr, *sf_end = nullptr, *sr_end = nullptr;
-  uint32_t *sf_word = nullptr, *sr_word = nullptr;
+        *car_r = nullptr, *sf_end = nullptr, *sr_end = nullptr, *sf_min = nullptr,
+        *sr_min = nullptr;
   if (g.nchunks > 1) {
     const size_t per = size_t(a.batch) * g.nchunks * NT * a.d_inner;
     const size_t sums = (size_t(a.batch) * g.nchunks * a.d_inner + 63) / 64 * 64;
@@ -1035,9 +975,9 @@ int launch_all(const S6Args &a, hipStream_t stream) {
     car_f = agg_r + per;
     car_r = car_f + per;
     sf_end = car_r + per;
-    sf_word = reinterpret_cast<uint32_t *>(sf_end + stats);
+    sf_min = sf_end + stats;
     sr_end = sf_end + 2 * stats;
-    sr_word = reinterpret_cast<uint32_t *>(sf_end + 3 * stats);
+    sr_min = sf_end + 3 * stats;
   }
   const T *u = static_cast<const T *>(a.u);
   const T *dl = static_cast<const T *>(a.delta);
@@ -1045,7 +985,7 @@ int launch_all(const S6Args &a, hipStream_t stream) {
   const T *C = static_cast<const T *>(a.C);
   hipLaunchKernelGGL((s6_chunk_kernel<T, NT, DX>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
                      u, dl, a.delta_bias, a.A, B, C, a.D, a.y, agg_s, agg_f, agg_r, sf_end,
-                     sf_word, sr_end, sr_word, g, a.direction);
+                     sf_min, sr_end, sr_min, g, a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 chunk launch")) return rc;
   if (g.nchunks == 1) return SSM_OK;
   const int parts = (g.nchunks + kCarryPart - 1) / kCarryPart;
@@ -1054,8 +994,8 @@ int launch_all(const S6Args &a, hipStream_t stream) {
                      agg_s, agg_f, agg_r, a.A, car_f, car_r, g, NT, a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 carry launch")) return rc;
   hipLaunchKernelGGL((s6_fix_kernel<T, NT, DX>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
-                     u, dl, a.delta_bias, a.A, B, C, a.D, a.y, car_f, car_r, sf_end, sf_word,
-                     sr_end, sr_word, g, a.direction);
+                     u, dl, a.delta_bias, a.A, B, C, a.D, a.y, car_f, car_r, sf_end, sf_min,
+                     sr_end, sr_min, g, a.direction);
   return hip_check(hipGetLastError(), "s6 fix launch");
 }
 
