@@ -222,6 +222,19 @@ def bench_copy(dev, steps, warmup):
     return 8.0 * n / (ms_kernel * 1e-3) / 1e9
 
 
+def bench_stream(dev, steps, warmup, n):
+    """The library's stream kernel, h = a * b over n floats: the linear
+    scan's 12 bytes per element with no recurrence, in the launch shape that
+    measured fastest for that traffic -- the rate the scan can approach."""
+    import torch
+    import mamba_s6_selective_amd as ssm
+    a = torch.empty(n, dtype=torch.float32, device=dev).uniform_(0.5, 1.0)
+    b = torch.empty(n, dtype=torch.float32, device=dev).normal_()
+    h = torch.empty_like(a)
+    _, ms_kernel = time_steps(lambda: ssm.stream_mul_f32(a, b, out=h), steps, warmup)
+    return LINEAR_BYTES_PER_ELEM * n / (ms_kernel * 1e-3) / 1e9, ms_kernel
+
+
 S6_BENCH = ["s6-fwd-b16-L1024-d256-N16-f32", "s6-fwd-b1-L65536-d1024-N16-bf16",
             "s6-bidir-b4-L8192-d1536-N16-bf16"]
 
@@ -243,7 +256,7 @@ def s6_algorithmic(w):
     return E, nbytes, E * w["N"], other
 
 
-def bench_s6(dev, name, steps, warmup, exp_cost):
+def bench_s6(dev, name, steps, warmup, exp_cost, extras=True):
     import torch
     import mamba_s6_selective_amd as ssm
     from mamba_s6_selective_amd.workloads import S6_WORKLOADS, s6_workload_inputs
@@ -267,7 +280,7 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
     ms_step, ms_kernel = time_steps(step, steps, warmup)
     extra = {}
     fused = None
-    if w["direction"] == "fwd" and w["dtype"] == "bf16":
+    if extras and w["direction"] == "fwd" and w["dtype"] == "bf16":
         # the same scan with delta given before its activation and softplus fused in
         pre = [inp.delta_pre.to(dev).clone() for _ in range(sets)]
         dl = [torch.empty_like(p) for p in pre]
@@ -299,9 +312,9 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
                  "separate_softplus_ms": round(ms_sp, 4),
                  "separate_softplus_then_scan_ms": round(ms_sep, 4),
                  "ratio_to_separate": round(ms_fused / ms_sep, 3)}
-        # The fix pass skips carry terms that are exactly zero and blocks whose
-        # correction rounds away, so its cost depends on how fast the states
-        # decay: with every term evaluated, and with A 64 times closer to 0.
+        # The fix pass leaves out carry terms once they are proven below 2^-24,
+        # so its cost depends on how fast the states decay: with every term
+        # evaluated, and with A 64 times closer to 0.
         os.environ["SSMSCAN_S6_FULL_FIX"] = "1"
         try:
             _, ms_full = time_steps(step, steps, warmup)
@@ -318,7 +331,7 @@ def bench_s6(dev, name, steps, warmup, exp_cost):
             "full_fix_ms": round(ms_full, 4), "ratio_full_fix": round(ms_full / ms_kernel, 3),
             "slow_decay_A": "-(n+1)/64", "slow_decay_ms": round(ms_slow, 4),
             "ratio_slow_decay": round(ms_slow / ms_kernel, 3)}
-    if w["direction"] == "bidir":
+    if extras and w["direction"] == "bidir":
         # the fused call against one forward and one reverse call on the same inputs
         def step_separate_dirs():
             t = bufs[k[0] % sets]
@@ -452,6 +465,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-s6", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="S6: time only the workload itself (no fused-softplus, full-fix, "
+                         "slow-decay or separate fwd + rev variants), so that a counter run "
+                         "sees only its launches")
     ap.add_argument("--s6-only", choices=S6_BENCH,
                     help="time only this S6 workload (for per-workload profiles) and print its record")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -476,7 +493,8 @@ def main():
         raise SystemExit("sentinel copy kernel did not reproduce its input; sweep discarded")
 
     if args.s6_only:
-        print(json.dumps(bench_s6(dev, args.s6_only, args.steps, args.warmup, args.exp_cost)),
+        print(json.dumps(bench_s6(dev, args.s6_only, args.steps, args.warmup, args.exp_cost,
+                                  extras=not args.no_extras)),
               flush=True)
         return
     copy_gbs = bench_copy(dev, 10, 3)
@@ -485,6 +503,9 @@ def main():
     alg_bytes = LINEAR_BYTES_PER_ELEM * n
     achieved = alg_bytes / (ms_kernel * 1e-3) / 1e9
     log(f"linear scan: {ms_kernel * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
+    stream_gbs, stream_ms = bench_stream(dev, args.steps, args.warmup, n)
+    log(f"stream reference: {stream_ms * 1e3:.1f} us/launch, {stream_gbs:.0f} GB/s; "
+        f"scan at {achieved / stream_gbs:.3f} of it")
     traffic = load_traffic("linear_scan", "linear_scan.hip", "scan_common.h")
     record = {
         "metric": "scan elements/s + achieved HBM GB/s (% of MI355X peak), linear & S6 fwd",
@@ -501,6 +522,12 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "copy_kernel_GBs": round(copy_gbs, 1),
+        "stream_reference": {"kernel": "stream_mul_kernel: h = a * b, 12 B/element, "
+                                       "one 16-byte vector per lane, 256 lanes per workgroup",
+                             "n": n, "ms_per_launch": round(stream_ms, 5),
+                             "achieved_GBs": round(stream_gbs, 1),
+                             "frac_of_8TBs": round(stream_gbs / HBM_PEAK_GBS, 4),
+                             "scan_frac_of_stream": round(achieved / stream_gbs, 4)},
     }
     record["linear_n65536"] = bench_linear_small(dev, args.steps, args.warmup)
     log(f"linear n=65536: {record['linear_n65536']['latency_us']} us per synchronised call")

@@ -267,6 +267,21 @@ SSM_API int ssm_selective_scan_fwd_ex(const void *u, const void *delta, const fl
  */
 SSM_API int ssm_copy_f32(const float *src, float *dst, int64_t n, void *stream);
 
+/*
+ * Device product h[i] = a[i] * b[i], i < n (fp32, IEEE products). The
+ * linear scan's HBM traffic -- two streams of n floats read, one written,
+ * 12 bytes per element -- without the recurrence, in the launch shape that
+ * measured fastest for that traffic on gfx950 (one 16-byte vector per lane,
+ * 256 lanes per workgroup, one workgroup per 4 KiB of each stream).
+ * Measurement code uses it as the attainable-bandwidth reference for the
+ * single-pass scan ("Selective-scan CUDA kernels" compares its scan with
+ * the memory system's rate in the same way).
+ * Errors: SSM_ERR_INVALID_ARG for n < 0, a null / misaligned pointer with
+ * n > 0, or h overlapping a or b; SSM_ERR_UNSUPPORTED for n > 2^40.
+ */
+SSM_API int ssm_stream_mul_f32(const float *a, const float *b, float *h, int64_t n,
+                               void *stream);
+
 /* Static English text for a status code. */
 SSM_API const char *ssm_status_string(int code);
 

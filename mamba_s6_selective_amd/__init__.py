@@ -36,6 +36,7 @@ SIGNATURES = {
     "ssm_selective_scan_fwd_ex": (ctypes.c_int, [_P] * 8 + [ctypes.c_int] * 5 +
                                   [ctypes.c_uint, _P]),
     "ssm_copy_f32": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+    "ssm_stream_mul_f32": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, _P]),
     "ssm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ssm_last_error": (ctypes.c_char_p, []),
     "ssm_release_workspace": (ctypes.c_int, []),
@@ -277,6 +278,27 @@ def copy_f32(src, dst):
     with torch.cuda.device(src.device):
         _check(lib.ssm_copy_f32(src.data_ptr(), dst.data_ptr(), src.numel(), _stream(src)))
     return dst
+
+
+def stream_mul_f32(a, b, out=None):
+    """out[:] = a * b (fp32 device tensors of equal size): the linear scan's
+    traffic without the recurrence, on the library's stream kernel."""
+    import torch
+    lib = load_library()
+    _dev_tensor(a, "a", (torch.float32,))
+    _dev_tensor(b, "b", (torch.float32,))
+    if a.numel() != b.numel():
+        raise ValueError("a and b sizes differ")
+    if out is None:
+        out = torch.empty_like(a)
+    _dev_tensor(out, "out", (torch.float32,))
+    if out.numel() != a.numel():
+        raise ValueError("out size differs from a")
+    _same_device(a=a, b=b, out=out)
+    with torch.cuda.device(a.device):
+        _check(lib.ssm_stream_mul_f32(a.data_ptr(), b.data_ptr(), out.data_ptr(), a.numel(),
+                                      _stream(a)))
+    return out
 
 
 def release_workspace():

@@ -75,6 +75,8 @@ size_t linear_noalloc_bytes();
 
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n,
                            hipStream_t stream);
+hipError_t launch_stream_mul_f32(const float *a, const float *b, float *h, int64_t n,
+                                 hipStream_t stream);
 
 // ---- three-pass linear recurrence ------------------------------------------
 

@@ -1069,6 +1069,35 @@ int linear_wgs_per_cu() {
   return plain < seg ? plain : seg;
 }
 
+// h = a * b elementwise: the linear scan's HBM traffic (two streams read,
+// one written) with no dependence between elements, as the attainable-rate
+// reference for the scan. One 16-byte vector per lane and one block of 256
+// vectors per workgroup: of the shapes measured for this traffic on gfx950
+// (grid-stride loops of 1024 to 16384 workgroups, persistent workgroups with
+// a tile in flight, 1 to 8 vectors per lane, 256 to 1024 lanes per
+// workgroup) the many short workgroups were fastest. The lane after the last
+// whole vector takes the 0 to 3 elements left.
+__global__ __launch_bounds__(256) void stream_mul_kernel(const float *__restrict__ a,
+                                                         const float *__restrict__ b,
+                                                         float *__restrict__ h, int64_t n) {
+  const int64_t nvec = n / 4;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < nvec) {
+    const float4 x = load_nt(a + 4 * i), y = load_nt(b + 4 * i);
+    store_nt(h + 4 * i, make_float4(x.x * y.x, x.y * y.y, x.z * y.z, x.w * y.w));
+  } else if (i == nvec) {
+    for (int64_t k = 4 * nvec; k < n; ++k) h[k] = a[k] * b[k];
+  }
+}
+
+hipError_t launch_stream_mul_f32(const float *a, const float *b, float *h, int64_t n,
+                                 hipStream_t stream) {
+  const int64_t blocks = (n / 4 + 1 + 255) / 256;  // the vectors and the tail lane
+  hipLaunchKernelGGL(stream_mul_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, a, b, h,
+                     n);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t stream) {
   int64_t blocks = (n / 4 + 255) / 256;
   if (blocks < 1) blocks = 1;

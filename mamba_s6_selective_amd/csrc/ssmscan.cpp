@@ -370,6 +370,21 @@ int ssm_copy_f32(const float *src, float *dst, int64_t n, void *stream) {
                    "copy launch");
 }
 
+int ssm_stream_mul_f32(const float *a, const float *b, float *h, int64_t n, void *stream) {
+  g_last_error.clear();
+  if (n < 0) return fail(SSM_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return SSM_OK;
+  if (n > (int64_t(1) << 40)) return fail(SSM_ERR_UNSUPPORTED, "n above 2^40");
+  if (!a || !b || !h) return fail(SSM_ERR_INVALID_ARG, "null pointer with n > 0");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(h))
+    return fail(SSM_ERR_INVALID_ARG, "a, b and h must be 16-byte aligned");
+  const size_t bytes = size_t(n) * sizeof(float);
+  if (overlap(h, bytes, a, bytes) || overlap(h, bytes, b, bytes))
+    return fail(SSM_ERR_INVALID_ARG, "h overlaps a or b");
+  return hip_check(launch_stream_mul_f32(a, b, h, n, static_cast<hipStream_t>(stream)),
+                   "stream launch");
+}
+
 static int s6_check(const void *u, const void *delta, const float *A, const void *B,
                     const void *C, const float *D, float *y, int batch, int L, int d_inner,
                     int N, int direction, size_t esize, bool *noop) {

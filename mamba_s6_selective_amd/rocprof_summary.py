@@ -1,7 +1,9 @@
 """Summaries of rocprofv3 output databases (rocpd SQLite) for profiles/.
 
-    python -m mamba_s6_selective_amd.rocprof_summary stats RUN_results.db ...
-        per-kernel call count and average / total duration (kernel trace)
+    python -m mamba_s6_selective_amd.rocprof_summary stats [--by-grid] RUN_results.db ...
+        per-kernel call count and average / total duration (kernel trace);
+        with --by-grid, one line per (kernel, grid size in work-items), so
+        that launches of one kernel on different problem sizes stay apart
 
     python -m mamba_s6_selective_amd.rocprof_summary counters RUN_results.db
         per-kernel median over dispatches of every counter the run collected
@@ -17,6 +19,8 @@
         the ratio of the bytes the copy kernel moves (copy_bytes read,
         copy_bytes written) to what the same counter reads for it.
         With --key NAME the record is merged into the --out file under NAME.
+        With --largest-grid only each kernel's dispatches of its largest grid
+        count (a run that also launches it on smaller problems).
 
     python -m mamba_s6_selective_amd.rocprof_summary valu VALU_results.db \\
         --kernel s6_chunk_kernel s6_carry_kernel s6_fix_kernel --tdn 1073741824 \\
@@ -46,26 +50,35 @@ def short_name(name: str) -> str:
     return name.split("(")[0]
 
 
-def kernel_stats(db: str):
+def kernel_stats(db: str, by_grid: bool = False):
+    """[(name, calls, total_us, avg_us)], longest total first."""
     con = sqlite3.connect(db)
-    rows = con.execute("select name, total_calls, total_duration, average from top_kernels")
-    return [(short_name(n), int(c), float(t), float(a)) for n, c, t, a in rows]
+    if not by_grid:
+        rows = con.execute("select name, total_calls, total_duration, average from top_kernels")
+        return [(short_name(n), int(c), float(t), float(a)) for n, c, t, a in rows]
+    rows = con.execute("select name, grid_x * grid_y * grid_z, count(*), sum(duration) "
+                       "from kernels group by name, grid_x, grid_y, grid_z")
+    out = [(f"{short_name(n)} [grid {g}]", int(c), float(t) / 1e3, float(t) / 1e3 / int(c))
+           for n, g, c, t in rows]
+    return sorted(out, key=lambda r: -r[2])
 
 
 def counter_per_dispatch(db: str, counter: str):
-    """{kernel short name: [value per dispatch]} for one counter."""
+    """{kernel short name: [(grid size, value) per dispatch]} for one counter."""
     con = sqlite3.connect(db)
     acc = defaultdict(float)
     names = {}
-    for kname, disp, cname, val in con.execute(
-            "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+    for kname, disp, grid, cname, val in con.execute(
+            "select kernel_name, dispatch_id, grid_size, counter_name, value "
+            "from counters_collection"):
         if cname != counter:
             continue
         acc[disp] += float(val)
-        names[disp] = short_name(kname)
+        names[disp] = (short_name(kname), int(grid))
     out = defaultdict(list)
     for disp, v in sorted(acc.items()):
-        out[names[disp]].append(v)
+        name, grid = names[disp]
+        out[name].append((grid, v))
     return out
 
 
@@ -77,10 +90,11 @@ def source_sha(*files: str) -> str:
 
 
 def cmd_stats(args):
-    print(f"{'kernel':<64} {'calls':>6} {'avg_us':>10} {'total_us':>12}")
+    width = 84 if args.by_grid else 64
+    print(f"{'kernel':<{width}} {'calls':>6} {'avg_us':>10} {'total_us':>12}")
     for db in args.dbs:
-        for name, calls, total, avg in kernel_stats(db):
-            print(f"{name[:64]:<64} {calls:>6} {avg:>10.2f} {total:>12.1f}")
+        for name, calls, total, avg in kernel_stats(db, args.by_grid):
+            print(f"{name[:width]:<{width}} {calls:>6} {avg:>10.2f} {total:>12.1f}")
 
 
 def cmd_counters(args):
@@ -91,23 +105,30 @@ def cmd_counters(args):
     kernels = sorted({k for d in per.values() for k in d})
     print(f"{'kernel':<64} " + " ".join(f"{c:>24}" for c in names))
     for k in kernels:
-        vals = [statistics.median(per[c][k]) if per[c].get(k) else float("nan") for c in names]
+        vals = [statistics.median(v for _, v in per[c][k]) if per[c].get(k) else float("nan")
+                for c in names]
         print(f"{k[:64]:<64} " + " ".join(f"{v:>24.4g}" for v in vals))
 
 
-def pick(d, key):
+def pick(d, key, largest_grid=False):
+    """Values of the dispatches of the first kernel whose name contains key
+    (only those of its largest grid with largest_grid)."""
     hits = [k for k in d if key in k]
     if not hits:
         raise SystemExit(f"no dispatches of a kernel matching {key!r}: {sorted(d)}")
-    return d[hits[0]]
+    disp = d[hits[0]]
+    if largest_grid:
+        top = max(g for g, _ in disp)
+        disp = [(g, v) for g, v in disp if g == top]
+    return [v for _, v in disp]
 
 
 def cmd_traffic(args):
     fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE")
     write = counter_per_dispatch(args.write, "WRITE_SIZE")
     # one kernel, or the sum over the kernels of one step
-    kf = sum(statistics.median(pick(fetch, k)) for k in args.kernel)
-    kw = sum(statistics.median(pick(write, k)) for k in args.kernel)
+    kf = sum(statistics.median(pick(fetch, k, args.largest_grid)) for k in args.kernel)
+    kw = sum(statistics.median(pick(write, k, args.largest_grid)) for k in args.kernel)
     cf = statistics.median(pick(fetch, COPY_KERNEL))
     cw = statistics.median(pick(write, COPY_KERNEL))
     f_scale = args.copy_bytes / (cf * 1024.0)
@@ -157,6 +178,7 @@ def main(argv=None):
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
+    s.add_argument("--by-grid", action="store_true")
     s.add_argument("dbs", nargs="+")
     c = sub.add_parser("counters")
     c.add_argument("db")
@@ -170,6 +192,7 @@ def main(argv=None):
                    help="csrc files the kernel is built from (hashed in this order)")
     t.add_argument("--out")
     t.add_argument("--key")
+    t.add_argument("--largest-grid", action="store_true")
     v = sub.add_parser("valu")
     v.add_argument("db")
     v.add_argument("--kernel", required=True, nargs="+", help="kernel names (substrings)")

@@ -89,6 +89,18 @@ def test_copy_argument_errors():
     assert lib.ssm_copy_f32(FAKE, FAKE, -4, None) == ssm.SSM_ERR_INVALID_ARG
 
 
+def test_stream_mul_argument_errors():
+    lib = ssm.load_library()
+    A, B, H = 0x100000, 0x200000, 0x300000
+    assert lib.ssm_stream_mul_f32(None, None, None, 0, None) == ssm.SSM_OK
+    assert lib.ssm_stream_mul_f32(A, B, None, 4, None) == ssm.SSM_ERR_INVALID_ARG
+    assert lib.ssm_stream_mul_f32(A, B, H, -4, None) == ssm.SSM_ERR_INVALID_ARG
+    assert lib.ssm_stream_mul_f32(A + 4, B, H, 4, None) == ssm.SSM_ERR_INVALID_ARG
+    assert lib.ssm_stream_mul_f32(A, B, B + 16, 16, None) == ssm.SSM_ERR_INVALID_ARG
+    assert b"overlaps" in lib.ssm_last_error()
+    assert lib.ssm_stream_mul_f32(A, B, H, (1 << 40) + 1, None) == ssm.SSM_ERR_UNSUPPORTED
+
+
 def test_binding_rejects_host_tensors():
     import torch
     a = torch.ones(8)

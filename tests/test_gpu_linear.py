@@ -184,3 +184,17 @@ def test_copy_sentinel():
     y = torch.empty_like(x)
     ssm.copy_f32(x, y)
     assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 1023, 1024, 1025, 4 * 256 + 3, 1000003, 1 << 22])
+def test_stream_mul_exact(n):
+    """The bandwidth reference kernel: h = a * b, each product the IEEE fp32
+    one (equal to the CPU's), at sizes with 0-3 tail elements and several
+    workgroups."""
+    say(f"stream mul n={n}")
+    dev = need_gpu()
+    g = torch.Generator().manual_seed(n)
+    a, b = torch.randn(n, generator=g), torch.randn(n, generator=g)
+    h = ssm.stream_mul_f32(a.to(dev), b.to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(h.cpu(), a * b)
