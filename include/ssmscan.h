@@ -198,6 +198,12 @@ SSM_API int ssm_linear_scan_hs(const float *a, const float *b, float h0, float *
  * y        : float[batch][L][d_inner], output (fp32).
  * direction: ssm_direction_t.
  * The (batch, L, d_inner, N) tensors dA, dBu and h never touch memory.
+ * Non-finite inputs give the inf and NaN positions (and signs) of the
+ * float64 recurrence: an exponential that flushes to zero in fp32 is kept as
+ * the smallest subnormal wherever it may meet an infinite state, and a chunk
+ * whose C holds an inf or NaN is evaluated again from its exact incoming
+ * states (C infinite makes sum_n C*(local + carry term) differ from the sum
+ * of the two parts).
  * Accuracy: with the sequence split into chunks, the carry into a chunk is
  * added as its exact decaying contribution, whose tail is left out once
  * proven below 2^-24 per group of 4 states over a block of steps: outputs
