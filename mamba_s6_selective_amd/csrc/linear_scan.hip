@@ -64,10 +64,10 @@ constexpr int kFan = 64;        // entries per look-back window
 
 // Tile shape: data waves per workgroup and float4 rows per wave. One
 // sequence: 8 x 4 rows = 8192 elements. The batched form spends more VALU per
-// element (segment positions, the reset policy) and runs 7-11 % faster with
-// more, shorter waves, 11 x 3 rows = 8448 elements (as many waves as fit the
-// register file, with the parked tiles within LDS); for one sequence that
-// shape is no faster.
+// element (segment positions, heads) and is fastest with more, shorter waves,
+// 11 x 3 rows = 8448 elements (as many waves as fit the register file, with
+// the parked tiles within LDS; 8 x 4: 320 against 301 us at 2^27, 9 x 4:
+// 312, 10 x 3: 306); for one sequence that shape is no faster.
 template <bool Seg>
 struct Shape {
   static constexpr int kWaves = Seg ? 11 : 8;

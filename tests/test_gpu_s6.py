@@ -247,11 +247,12 @@ def test_s6_zero_B_gives_skip_only():
 
 @pytest.mark.parametrize("chunk", ["256", "1024"])
 def test_s6_decayed_carry_terms(chunk, monkeypatch):
-    """The fix pass skips a group of states for a block once every lane's carry
-    term there is exactly zero. States decay at very different rates here, the
-    slow ones sit in different groups per test row, one channel keeps a group
-    alive that every other channel has let die, and one group has A > 0 (never
-    skipped); a wrongly skipped group would add an O(1) error."""
+    """The fix pass leaves a group of states out of a block once every lane's
+    carry terms there are proven below 2^-24. States decay at very different
+    rates here, the slow ones sit in different groups per test row, one
+    channel keeps a group alive that every other channel has let die, and one
+    group has A > 0 (never left out); a wrongly dropped group would add an
+    O(1) error."""
     say(f"s6 decayed carry terms chunk={chunk}")
     monkeypatch.setenv("SSMSCAN_S6_CHUNK", chunk)
     inp = s6_inputs(2, 3000, 128, 16, seed=515, dtype="f32")
