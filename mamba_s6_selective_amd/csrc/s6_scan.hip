@@ -551,12 +551,14 @@ constexpr float kTruncScale = 1.01f / kTruncGroup;  // margin / kTruncGroup
 template <int NT>
 struct FixGroups {
   static constexpr int kCount = (NT + kFixGroup - 1) / kFixGroup;
-  float Ag[kCount];    // largest Ap[n] of the group
-  float cabs[kCount];  // sum of |cin[n]| over the group
-  bool keep[kCount];   // never left out: a non-finite carry, a NaN or non-negative Ap
+  float Ag[kCount];     // largest Ap[n] of the group
+  float cabs[kCount];   // sum of |cin[n]| over the group
+  bool keep[kCount];    // never left out: a non-finite carry, a NaN or non-negative Ap
+  float sdead[kCount];  // smallest running sum at which the group was left out (NaN: never)
   __device__ __forceinline__ FixGroups(const float (&Ap)[NT], const float (&cin)[NT]) {
 #pragma unroll
     for (int g = 0; g < kCount; ++g) {
+      sdead[g] = __builtin_nanf("");
       float ag = -__builtin_inff(), ca = 0.0f;
       bool k = false;
 #pragma unroll
@@ -576,14 +578,23 @@ struct FixGroups {
   // Decides a block of kPrefetch steps from the chunk pass's smallest
   // running sum over it: bit g set when group g has a lane that needs its
   // terms (0: the block leaves y as it is). cscale = maxC * kTruncScale.
-  __device__ __forceinline__ uint32_t decide(float smin, float cscale) const {
+  // Blocks are decided in sweep order. The bound only shrinks as the
+  // smallest running sum grows (cabs, Ag < 0 and cscale are fixed for the
+  // sweep), so a group left out at smallest sum s stays out for a block
+  // whose smallest sum is at least s in every lane, without its
+  // exponential; otherwise (a negative delta, a NaN) the bound is evaluated.
+  __device__ __forceinline__ uint32_t decide(float smin, float cscale) {
     const bool ok = smin >= 0.0f;  // false for a NaN or a negative sum
     uint32_t m = 0;
 #pragma unroll
     for (int g = 0; g < kCount; ++g) {
+      if (__builtin_amdgcn_ballot_w64(!(smin >= sdead[g])) == 0) continue;  // still out
       const float bound = cabs[g] * exp2_hw(Ag[g] * smin) * cscale;
       const bool drop = ok && !keep[g] && bound <= 1.0f;  // false for a NaN bound
-      if (__builtin_amdgcn_ballot_w64(!drop) != 0) m |= 1u << g;
+      if (__builtin_amdgcn_ballot_w64(!drop) != 0)
+        m |= 1u << g;
+      else
+        sdead[g] = fminf(sdead[g], smin);  // fminf(NaN, s) = s
     }
     return m;
   }
@@ -698,7 +709,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   const uint32_t yo = uint32_t(d) * 4u;
   const size_t s0 = stat_index(g, b, c, 0, d);
   const size_t ss = size_t(g.d_inner);  // stride between blocks of the statistics
-  const FixGroups<NT> groups(Ap, cin);
+  FixGroups<NT> groups(Ap, cin);
   // A non-finite carry: its terms go through exp2_nz, so that an infinite
   // carry times an exponential that flushed to zero stays infinite (rare).
   bool nonfinite = false;
@@ -860,7 +871,7 @@ __device__ void recompute_chunk(const T *__restrict__ u, const T *__restrict__ d
 }
 
 template <typename T, int NT, class DX>
-__global__ __launch_bounds__(kThreads) void s6_fix_kernel(
+__global__ __launch_bounds__(kThreads, 4) void s6_fix_kernel(
     const T *__restrict__ u, const T *__restrict__ delta, const float *__restrict__ dbias,
     const float *__restrict__ A, const T *__restrict__ B, const T *__restrict__ C,
     const float *__restrict__ D, float *__restrict__ y, const float *__restrict__ carry_f,
