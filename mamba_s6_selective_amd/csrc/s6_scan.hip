@@ -52,6 +52,16 @@ __device__ __forceinline__ float ldv(const float *p) { return *p; }
 __device__ __forceinline__ float ldv(const uint16_t *p) {
   return __uint_as_float(uint32_t(*p) << 16);
 }
+// A u or delta word as loaded (fp32 bits, or a bf16 value zero-extended),
+// for words fetched a block of steps ahead: they are widened to fp32 only
+// where they are used (widen). Widening at the load makes the wave wait for
+// the load right there, which is what fetching ahead is meant to avoid.
+__device__ __forceinline__ uint32_t ldw(const float *p) { return __float_as_uint(*p); }
+__device__ __forceinline__ uint32_t ldw(const uint16_t *p) { return *p; }
+template <typename T>
+__device__ __forceinline__ float widen(uint32_t w) {
+  return __uint_as_float(sizeof(T) == 2 ? w << 16 : w);
+}
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -233,6 +243,20 @@ __device__ __forceinline__ uint32_t touch_rows(const T *__restrict__ B, const T 
     return uint32_t(v);
 }
 __device__ __forceinline__ void keep_alive(uint32_t v) { asm volatile("" ::"v"(v)); }
+// Marks x as rewritten here (no instruction), so that the computation of x
+// stays before this point instead of moving to its uses.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+
+// A sweep keeps the words it fetches a block ahead as loaded and widens them
+// where the block uses them (widened at the load, the wave waits for the load
+// right there), except the accumulating sweep: its y words leave no room for
+// it, and the kernel then spilled and ran slower. The u words are pinned where
+// they are widened unless delta goes through softplus, whose evaluation needs
+// those registers (each choice the faster one measured on gfx950).
+template <bool Accumulate>
+constexpr bool kWidenAtUse = !Accumulate;
+template <bool Accumulate, class DX>
+constexpr bool kPinU = !Accumulate && std::is_same<DX, DeltaAsIs>::value;
 
 struct SweepStats {
   float *s_end;
@@ -277,8 +301,15 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
   // block being computed while the next block's loads land in the other,
   // and the loop runs two blocks per iteration so the sets trade roles
   // without copies.
-  float ad[kPrefetch], ax[kPrefetch], ay[kPrefetch];
-  float bd[kPrefetch], bx[kPrefetch], by[kPrefetch];
+  uint32_t ad[kPrefetch], ax[kPrefetch], bd[kPrefetch], bx[kPrefetch];
+  float ay[kPrefetch], by[kPrefetch];
+  // The words kept as loaded and widened where the block uses them (at_use),
+  // or widened at the load.
+  constexpr bool at_use = kWidenAtUse<Accumulate>;
+  auto fetch = [&](const T *q) -> uint32_t {
+    return at_use ? ldw(q) : __float_as_uint(ldv(q));
+  };
+  auto take = [&](uint32_t w) -> float { return at_use ? widen<T>(w) : __uint_as_float(w); };
   // Lowest row of the block of steps starting at sweep index i.
   auto block_row = [&](int i) { return row0 + tof(Reverse ? i + kPrefetch - 1 : i); };
   uint32_t touched = 0;
@@ -287,42 +318,51 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       const size_t r = row(j);
-      ad[j] = ldv(&at(delta + r, io));
-      ax[j] = ldv(&at(u + r, io));
+      ad[j] = fetch(&at(delta + r, io));
+      ax[j] = fetch(&at(u + r, io));
       if (Accumulate) ay[j] = at(y + r, yo);
     }
   }
-  // One block of kPrefetch steps from sweep index i0, its words in (rd, cx,
+  // One block of kPrefetch steps from sweep index i0, its words in (rd, rx,
   // cy); the next block's words are loaded into (nd, nx, ny).
-  auto block = [&](int i0, const float (&rd)[kPrefetch], const float (&cx)[kPrefetch],
-                   const float (&cy)[kPrefetch], float (&nd)[kPrefetch], float (&nx)[kPrefetch],
-                   float (&ny)[kPrefetch]) {
-    float cd[kPrefetch];
+  auto block = [&](int i0, const uint32_t (&rd)[kPrefetch], const uint32_t (&rx)[kPrefetch],
+                   const float (&cy)[kPrefetch], uint32_t (&nd)[kPrefetch],
+                   uint32_t (&nx)[kPrefetch], float (&ny)[kPrefetch]) {
+    // Widened and transformed when used: their loads have had a block of
+    // steps to land. A pinned u word is widened here, not next to a use that
+    // comes after the next block's loads.
+    float cd[kPrefetch], cx[kPrefetch];
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j)
-      cd[j] = dx(rd[j]);  // transformed when used: its load has had a block of steps to land
-    keep_alive(touched);  // issued a block ago, with the loads just consumed
-    if (i0 + kPrefetch < full) {
-#pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) {
-        const size_t rn = row(i0 + kPrefetch + j);
-        nd[j] = ldv(&at(delta + rn, io));
-        nx[j] = ldv(&at(u + rn, io));
-        if (Accumulate) ny[j] = at(y + rn, yo);
-      }
-      touched = touch_rows<T, NT>(B, C, block_row(i0 + kPrefetch) * NT);
+    for (int j = 0; j < kPrefetch; ++j) {
+      cd[j] = dx(take(rd[j]));
+      cx[j] = take(rx[j]);
+      if (kPinU<Accumulate, DX>) pin(cx[j]);
     }
-    float smin = 0.0f;
     // A step's exponential can flush to zero only if delta*A*log2(e) < -126
     // (|delta*A| > 87); decided per block from the largest delta (an infinite
     // one included). Such a block runs step by step with exp2_nz, so that an
     // infinite state stays infinite as in the float64 recurrence: a compact
     // loop that reads its words again (a second unrolled copy of the block
-    // spilled registers in the common path).
+    // spilled registers in the common path). Decided before the next block's
+    // loads are issued, so the wait for this block's words is not a wait for
+    // those.
     float dmax = cd[0];
 #pragma unroll
     for (int j = 1; j < kPrefetch; ++j) dmax = fmaxf(dmax, cd[j]);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(dmax * ap_min < -126.0f) != 0, 0)) {
+    const bool careful = __builtin_amdgcn_ballot_w64(dmax * ap_min < -126.0f) != 0;
+    keep_alive(touched);  // issued a block ago, with the words just consumed
+    if (i0 + kPrefetch < full) {
+#pragma unroll
+      for (int j = 0; j < kPrefetch; ++j) {
+        const size_t rn = row(i0 + kPrefetch + j);
+        nd[j] = fetch(&at(delta + rn, io));
+        nx[j] = fetch(&at(u + rn, io));
+        if (Accumulate) ny[j] = at(y + rn, yo);
+      }
+      touched = touch_rows<T, NT>(B, C, block_row(i0 + kPrefetch) * NT);
+    }
+    float smin = 0.0f;
+    if (__builtin_expect(careful, 0)) {
 #pragma unroll 1
       for (int j = 0; j < kPrefetch; ++j) {
         const size_t r = row(i0 + j);
@@ -716,32 +756,44 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
 #pragma unroll
   for (int n = 0; n < NT; ++n) nonfinite = nonfinite || !__builtin_isfinite(cin[n]);
   const bool careful = __builtin_amdgcn_ballot_w64(nonfinite) != 0;
-  // Loads what block k needs into (dr, yr, s_in): its delta and y words and
-  // the running sum before it.
-  // The loads also bring the block's C rows toward L2 (touched, held until
-  // the block runs), ahead of its scalar row loads.
-  auto load_block = [&](int k, float (&dr)[kPrefetch], float (&yr)[kPrefetch], float &s_in,
-                        uint32_t &touched) {
-    touched = touch_rows<T, NT>(
+  // The words one live block needs: its delta words (widened when the block
+  // runs), its y words, the running sum before it, and the value of a load
+  // that brings its C rows toward L2 ahead of its scalar row loads (held
+  // until the block runs).
+  struct Words {
+    uint32_t d[kPrefetch];
+    float yv[kPrefetch];
+    float s_in;
+    uint32_t touched;
+  };
+  auto load_block = [&](int k, Words &w) {
+    w.touched = touch_rows<T, NT>(
         C, C, (row0 + tof(Reverse ? k * kPrefetch + kPrefetch - 1 : k * kPrefetch)) * NT);
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      dr[j] = ldv(&at(delta + row(k * kPrefetch + j), io));
-      yr[j] = at(y + row(k * kPrefetch + j), yo);
+      w.d[j] = ldw(&at(delta + row(k * kPrefetch + j), io));
+      w.yv[j] = at(y + row(k * kPrefetch + j), yo);
     }
-    s_in = k > 0 ? s_end[s0 + size_t(k - 1) * ss] : 0.0f;
+    w.s_in = k > 0 ? s_end[s0 + size_t(k - 1) * ss] : 0.0f;
   };
-  // Evaluates block k from its loaded words for the groups in live.
-  auto run_block = [&](int k, const float (&dr)[kPrefetch], const float (&yr)[kPrefetch],
-                       float S, uint32_t live, uint32_t touched) {
-    keep_alive(touched);
-    const float S_in = S;  // the running sum before the block
+  // Evaluates block k from its words (cur) for the groups in live, and loads
+  // the words of the next block that changes y (knext, none if negative) into
+  // nxt. cur's words are all taken up before those loads are issued: a wait
+  // for one of them placed after the loads would wait for the loads as well.
+  auto run_block = [&](int k, Words &cur, int knext, Words &nxt, uint32_t live) {
+    float S_in = cur.s_in;  // the running sum before the block
     float Sj[kPrefetch];
+    float S = S_in;
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      S += dx(dr[j]);
+      S += dx(widen<T>(cur.d[j]));
       Sj[j] = S;
+      pin(Sj[j]);
+      pin(cur.yv[j]);
     }
+    pin(S_in);
+    keep_alive(cur.touched);
+    if (knext >= 0) load_block(knext, nxt);
     const int i0 = k * kPrefetch;
     if (__builtin_expect(careful, false)) {
       // Rare (a non-finite carry): step by step with exp2_nz, reading delta
@@ -766,7 +818,7 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
         wait_scalar_loads();
         if (j + 1 < kPrefetch) Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
         at(y + row(i0 + j), yo) =
-            yr[j] + fix_step<T, NT, true, false>(Sj[j], Cc, Ap, cin, live);
+            cur.yv[j] + fix_step<T, NT, true, false>(Sj[j], Cc, Ap, cin, live);
         if (j + 1 < kPrefetch) Cc = Cn;
       }
     }
@@ -792,28 +844,26 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
     }
     if (masks == 0) continue;  // wave-uniform: the whole window leaves y as it is
     // Its blocks that change y, each one's words loaded while the one before
-    // it computes.
+    // it computes; two blocks per iteration, so that the two word sets trade
+    // roles without copies.
     int i = __builtin_ctz(masks) / 4;
-    float dr[kPrefetch], yr[kPrefetch], s_in;
-    uint32_t tr;
-    load_block(w0 + i, dr, yr, s_in, tr);
-    for (;;) {
-      const uint32_t live = (masks >> (4 * i)) & 0xfu;
+    Words wa, wb;
+    load_block(w0 + i, wa);
+    auto next_live = [&](uint32_t &live) {
+      live = (masks >> (4 * i)) & 0xfu;
       masks &= ~(0xfu << (4 * i));
-      const int inext = masks ? __builtin_ctz(masks) / 4 : -1;
-      float dn[kPrefetch], yn[kPrefetch], sn = 0.0f;
-      uint32_t tn = 0;
-      if (inext >= 0) load_block(w0 + inext, dn, yn, sn, tn);
-      run_block(w0 + i, dr, yr, s_in, live, tr);
+      return masks ? __builtin_ctz(masks) / 4 : -1;
+    };
+    for (;;) {
+      uint32_t live;
+      int inext = next_live(live);
+      run_block(w0 + i, wa, inext >= 0 ? w0 + inext : -1, wb, live);
       if (inext < 0) break;
       i = inext;
-#pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) {
-        dr[j] = dn[j];
-        yr[j] = yn[j];
-      }
-      s_in = sn;
-      tr = tn;
+      inext = next_live(live);
+      run_block(w0 + i, wb, inext >= 0 ? w0 + inext : -1, wa, live);
+      if (inext < 0) break;
+      i = inext;
     }
   }
   float S = nfull > 0 ? s_end[s0 + size_t(nfull - 1) * ss] : 0.0f;
