@@ -247,17 +247,6 @@ __device__ __forceinline__ void keep_alive(uint32_t v) { asm volatile("" ::"v"(v
 // stays before this point instead of moving to its uses.
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
-// A sweep keeps the words it fetches a block ahead as loaded and widens them
-// where the block uses them (widened at the load, the wave waits for the load
-// right there), except the accumulating sweep: its y words leave no room for
-// it, and the kernel then spilled and ran slower. The u words are pinned where
-// they are widened unless delta goes through softplus, whose evaluation needs
-// those registers (each choice the faster one measured on gfx950).
-template <bool Accumulate>
-constexpr bool kWidenAtUse = !Accumulate;
-template <bool Accumulate, class DX>
-constexpr bool kPinU = !Accumulate && std::is_same<DX, DeltaAsIs>::value;
-
 struct SweepStats {
   float *s_end;
   float *s_min;
@@ -270,9 +259,12 @@ struct SweepStats {
 // branch inside a block (so the compiler can overlap neighbouring steps), and
 // each lane's words for the next block are loaded while the current block
 // computes; B[t] and C[t] are wave-uniform scalar loads. A tail of fewer than
-// kPrefetch steps runs one step at a time.
+// kPrefetch steps runs one step at a time, with exp2_nz.
+// Returns true (the same in every lane) when a block's exponential may have
+// flushed to zero: then y, h and S are not to be used, and careful_sweep
+// evaluates the chunk again (the statistics stand: they depend on delta alone).
 template <typename T, int NT, bool Reverse, bool Accumulate, class DX>
-__device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__restrict__ delta,
+__device__ __forceinline__ bool chunk_sweep(const T *__restrict__ u, const T *__restrict__ delta,
                                             const T *__restrict__ B, const T *__restrict__ C,
                                             float *__restrict__ y, const float (&Ap)[NT],
                                             float Dd, const DX &dx, const Geometry &g, int b,
@@ -301,25 +293,21 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
   // block being computed while the next block's loads land in the other,
   // and the loop runs two blocks per iteration so the sets trade roles
   // without copies.
+  // The delta and u words stay as loaded until the block that uses them
+  // widens them (ldw, widen).
   uint32_t ad[kPrefetch], ax[kPrefetch], bd[kPrefetch], bx[kPrefetch];
   float ay[kPrefetch], by[kPrefetch];
-  // The words kept as loaded and widened where the block uses them (at_use),
-  // or widened at the load.
-  constexpr bool at_use = kWidenAtUse<Accumulate>;
-  auto fetch = [&](const T *q) -> uint32_t {
-    return at_use ? ldw(q) : __float_as_uint(ldv(q));
-  };
-  auto take = [&](uint32_t w) -> float { return at_use ? widen<T>(w) : __uint_as_float(w); };
   // Lowest row of the block of steps starting at sweep index i.
   auto block_row = [&](int i) { return row0 + tof(Reverse ? i + kPrefetch - 1 : i); };
   uint32_t touched = 0;
+  bool flushes = false;  // this lane's deltas may flush an exponential to zero
   if (full > 0) {
     touched = touch_rows<T, NT>(B, C, block_row(0) * NT);
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       const size_t r = row(j);
-      ad[j] = fetch(&at(delta + r, io));
-      ax[j] = fetch(&at(u + r, io));
+      ad[j] = ldw(&at(delta + r, io));
+      ax[j] = ldw(&at(u + r, io));
       if (Accumulate) ay[j] = at(y + r, yo);
     }
   }
@@ -329,78 +317,60 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
                    const float (&cy)[kPrefetch], uint32_t (&nd)[kPrefetch],
                    uint32_t (&nx)[kPrefetch], float (&ny)[kPrefetch]) {
     // Widened and transformed when used: their loads have had a block of
-    // steps to land. A pinned u word is widened here, not next to a use that
-    // comes after the next block's loads.
+    // steps to land. The u words are widened here (pinned), not next to a
+    // use that comes after the next block's loads.
     float cd[kPrefetch], cx[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      cd[j] = dx(take(rd[j]));
-      cx[j] = take(rx[j]);
-      if (kPinU<Accumulate, DX>) pin(cx[j]);
+      cd[j] = dx(widen<T>(rd[j]));
+      cx[j] = widen<T>(rx[j]);
+      pin(cx[j]);
     }
     // A step's exponential can flush to zero only if delta*A*log2(e) < -126
-    // (|delta*A| > 87); decided per block from the largest delta (an infinite
-    // one included). Such a block runs step by step with exp2_nz, so that an
-    // infinite state stays infinite as in the float64 recurrence: a compact
-    // loop that reads its words again (a second unrolled copy of the block
-    // spilled registers in the common path). Decided before the next block's
-    // loads are issued, so the wait for this block's words is not a wait for
-    // those.
+    // (|delta*A| > 87); noted per block from the largest delta (an infinite
+    // one included), before the next block's loads are issued, so the wait
+    // for this block's words is not a wait for those. Such a chunk is
+    // evaluated again step by step (careful_sweep): a branch to a step-by-step
+    // block here cost the common path registers.
     float dmax = cd[0];
 #pragma unroll
     for (int j = 1; j < kPrefetch; ++j) dmax = fmaxf(dmax, cd[j]);
-    const bool careful = __builtin_amdgcn_ballot_w64(dmax * ap_min < -126.0f) != 0;
+    flushes = flushes || dmax * ap_min < -126.0f;
     keep_alive(touched);  // issued a block ago, with the words just consumed
     if (i0 + kPrefetch < full) {
 #pragma unroll
       for (int j = 0; j < kPrefetch; ++j) {
         const size_t rn = row(i0 + kPrefetch + j);
-        nd[j] = fetch(&at(delta + rn, io));
-        nx[j] = fetch(&at(u + rn, io));
+        nd[j] = ldw(&at(delta + rn, io));
+        nx[j] = ldw(&at(u + rn, io));
         if (Accumulate) ny[j] = at(y + rn, yo);
       }
       touched = touch_rows<T, NT>(B, C, block_row(i0 + kPrefetch) * NT);
     }
     float smin = 0.0f;
-    if (__builtin_expect(careful, 0)) {
-#pragma unroll 1
-      for (int j = 0; j < kPrefetch; ++j) {
-        const size_t r = row(i0 + j);
-        const float dt = dx(ldv(&at(delta + r, io)));
-        Row<T, NT> Bc, Cc;
-        Bc.load(B + (row0 + tof(i0 + j)) * NT);
-        Cc.load(C + (row0 + tof(i0 + j)) * NT);
-        const float out = s6_step<T, NT, true>(dt, ldv(&at(u + r, io)), Bc, Cc, Ap, Dd, h);
-        float &yr = at(y + r, yo);
-        yr = Accumulate ? yr + out : out;
-        S += dt;
-        smin = j == 0 ? S : fminf(smin, S);
-      }
-    } else {
-      // B/C rows go one step ahead: step j's rows were loaded during step j-1.
-      Row<T, NT> Bc, Cc;
-      Bc.load(B + (row0 + tof(i0)) * NT);
-      Cc.load(C + (row0 + tof(i0)) * NT);
+    // B/C rows go one step ahead: step j's rows were loaded during step j-1.
+    Row<T, NT> Bc, Cc;
+    Bc.load(B + (row0 + tof(i0)) * NT);
+    Cc.load(C + (row0 + tof(i0)) * NT);
 #pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) {
-        Row<T, NT> Bn, Cn;
-        wait_scalar_loads();
-        if (j + 1 < kPrefetch) {
-          Bn.load(B + (row0 + tof(i0 + j + 1)) * NT);
-          Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
-        }
-        // Keeps the next rows' loads at the head of the step: left to itself the
-        // scheduler may sink them (with their address arithmetic) to just before
-        // the next wait, which then waits for the whole scalar-load latency.
-        __builtin_amdgcn_sched_barrier(0);
-        const float out = s6_step<T, NT>(cd[j], cx[j], Bc, Cc, Ap, Dd, h);
-        at(y + row(i0 + j), yo) = Accumulate ? cy[j] + out : out;
-        S += cd[j];
-        smin = j == 0 ? S : fminf(smin, S);
-        if (j + 1 < kPrefetch) {
-          Bc = Bn;
-          Cc = Cn;
-        }
+    for (int j = 0; j < kPrefetch; ++j) {
+      Row<T, NT> Bn, Cn;
+      wait_scalar_loads();
+      if (j + 1 < kPrefetch) {
+        Bn.load(B + (row0 + tof(i0 + j + 1)) * NT);
+        Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
+      }
+      // Keeps the next rows' loads at the head of the step: left to itself the
+      // scheduler may sink them (with their address arithmetic) to just before
+      // the next wait, which then waits for the whole scalar-load latency.
+      __builtin_amdgcn_sched_barrier(0);
+      const float out = s6_step<T, NT>(cd[j], cx[j], Bc, Cc, Ap, Dd, h);
+      at(y + row(i0 + j), yo) = Accumulate ? cy[j] + out : out;
+      S += cd[j];
+      smin = j == 0 ? S : fminf(smin, S);
+      if (j + 1 < kPrefetch) {
+        Bc = Bn;
+        Cc = Cn;
       }
     }
     if (stats) {  // wave-uniform
@@ -425,6 +395,40 @@ __device__ __forceinline__ void chunk_sweep(const T *__restrict__ u, const T *__
     Bc.load(B + (row0 + t) * NT);
     Cc.load(C + (row0 + t) * NT);
     const float out = s6_step<T, NT, true>(dt, x, Bc, Cc, Ap, Dd, h);
+    float &yr = at(y + r, yo);
+    yr = Accumulate ? yr + out : out;
+    S += dt;
+  }
+  return __builtin_amdgcn_ballot_w64(flushes) != 0;
+}
+
+// The chunk-local recurrence from a zero state, step by step with exp2_nz,
+// so that an infinite state stays infinite as in the float64 recurrence
+// where a fast sweep's exponential may have flushed to zero (rare: delta*|A|
+// above 87 in the chunk). The same arithmetic as chunk_sweep otherwise, so
+// the same y, h and S.
+template <typename T, int NT, bool Reverse, bool Accumulate, class DX>
+__device__ __forceinline__ void careful_sweep(const T *__restrict__ u,
+                                              const T *__restrict__ delta,
+                                              const T *__restrict__ B, const T *__restrict__ C,
+                                              float *__restrict__ y, const float (&Ap)[NT],
+                                              float Dd, const DX &dx, const Geometry &g, int b,
+                                              int d, int t0, int t1, float (&h)[NT], float &S) {
+#pragma unroll
+  for (int n = 0; n < NT; ++n) h[n] = 0.0f;
+  S = 0.0f;
+  const size_t row0 = size_t(b) * g.L;
+  const uint32_t io = uint32_t(d) * uint32_t(sizeof(T));
+  const uint32_t yo = uint32_t(d) * 4u;
+#pragma unroll 1
+  for (int i = 0; i < t1 - t0; ++i) {
+    const int t = Reverse ? (t1 - 1 - i) : (t0 + i);
+    const size_t r = (row0 + t) * size_t(g.d_inner);
+    const float dt = dx(ldv(&at(delta + r, io)));
+    Row<T, NT> Bc, Cc;
+    Bc.load(B + (row0 + t) * NT);
+    Cc.load(C + (row0 + t) * NT);
+    const float out = s6_step<T, NT, true>(dt, ldv(&at(u + r, io)), Bc, Cc, Ap, Dd, h);
     float &yr = at(y + r, yo);
     yr = Accumulate ? yr + out : out;
     S += dt;
@@ -456,8 +460,9 @@ __global__ __launch_bounds__(kThreads, 4) void s6_chunk_kernel(
   const SweepStats stf{sf_end, multi ? sf_min : nullptr};
   const SweepStats str{sr_end, multi ? sr_min : nullptr};
   if (direction != SSM_DIR_REV) {
-    chunk_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1, h, S,
-                                     stf);
+    if (chunk_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1, h,
+                                         S, stf))
+      careful_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, h, S);
     if (multi) {
       agg_s[sum_index(g, b, c, d)] = S;
 #pragma unroll
@@ -465,12 +470,20 @@ __global__ __launch_bounds__(kThreads, 4) void s6_chunk_kernel(
     }
   }
   if (direction != SSM_DIR_FWD) {
-    if (direction == SSM_DIR_BIDIR)
-      chunk_sweep<T, NT, true, true>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1, h, S,
-                                     str);
-    else
-      chunk_sweep<T, NT, true, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1, h, S,
-                                      str);
+    if (direction == SSM_DIR_BIDIR) {
+      if (chunk_sweep<T, NT, true, true>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1, h,
+                                         S, str)) {
+        // The sweep has added to y what it must not have: y is formed again
+        // by the forward sweep, then the reverse one adds its own.
+        float hf[NT], sf;
+        careful_sweep<T, NT, false, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, hf,
+                                           sf);
+        careful_sweep<T, NT, true, true>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, h, S);
+      }
+    } else if (chunk_sweep<T, NT, true, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, c, d, t0, t1,
+                                               h, S, str)) {
+      careful_sweep<T, NT, true, false>(u, delta, B, C, y, Ap, Dd, dx, g, b, d, t0, t1, h, S);
+    }
     if (multi) {
       if (direction == SSM_DIR_REV) agg_s[sum_index(g, b, c, d)] = S;
 #pragma unroll
@@ -750,12 +763,27 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
   const size_t s0 = stat_index(g, b, c, 0, d);
   const size_t ss = size_t(g.d_inner);  // stride between blocks of the statistics
   FixGroups<NT> groups(Ap, cin);
-  // A non-finite carry: its terms go through exp2_nz, so that an infinite
-  // carry times an exponential that flushed to zero stays infinite (rare).
+  // A non-finite carry (rare): every step with every group, one step at a
+  // time with exp2_nz, so that an infinite carry times an exponential that
+  // flushed to zero stays infinite; the running sum is formed again from the
+  // chunk's entry point (the same additions as the chunk pass, so the same
+  // sums). Kept out of the loop below, where a branch to it cost registers.
   bool nonfinite = false;
 #pragma unroll
   for (int n = 0; n < NT; ++n) nonfinite = nonfinite || !__builtin_isfinite(cin[n]);
-  const bool careful = __builtin_amdgcn_ballot_w64(nonfinite) != 0;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(nonfinite) != 0, 0)) {
+    float S = 0.0f;
+#pragma unroll 1
+    for (int i = 0; i < len; ++i) {
+      const size_t r = row(i);
+      S += dx(ldv(&at(delta + r, io)));
+      Row<T, NT> Cc;
+      Cc.load(C + (row0 + tof(i)) * NT);
+      float &yr = at(y + r, yo);
+      yr = yr + fix_step<T, NT, false, true>(S, Cc, Ap, cin, 0);
+    }
+    return;
+  }
   // The words one live block needs: its delta words (widened when the block
   // runs), its y words, the running sum before it, and the value of a load
   // that brings its C rows toward L2 ahead of its scalar row loads (held
@@ -776,51 +804,33 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
     }
     w.s_in = k > 0 ? s_end[s0 + size_t(k - 1) * ss] : 0.0f;
   };
-  // Evaluates block k from its words (cur) for the groups in live, and loads
-  // the words of the next block that changes y (knext, none if negative) into
-  // nxt. cur's words are all taken up before those loads are issued: a wait
-  // for one of them placed after the loads would wait for the loads as well.
-  auto run_block = [&](int k, Words &cur, int knext, Words &nxt, uint32_t live) {
-    float S_in = cur.s_in;  // the running sum before the block
-    float Sj[kPrefetch];
-    float S = S_in;
+  // Takes up a block's words (the running sum at each of its steps, its y
+  // words): the waits for its loads fall here.
+  auto take_up = [&](Words &w, float (&Sj)[kPrefetch], float (&yv)[kPrefetch]) {
+    float S = w.s_in;  // the running sum before the block
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
-      S += dx(widen<T>(cur.d[j]));
+      S += dx(widen<T>(w.d[j]));
       Sj[j] = S;
       pin(Sj[j]);
-      pin(cur.yv[j]);
+      yv[j] = w.yv[j];
+      pin(yv[j]);
     }
-    pin(S_in);
-    keep_alive(cur.touched);
-    if (knext >= 0) load_block(knext, nxt);
+    keep_alive(w.touched);
+  };
+  // Evaluates block k from its taken-up values for the groups in live.
+  auto run_block = [&](int k, const float (&Sj)[kPrefetch], const float (&yv)[kPrefetch],
+                       uint32_t live) {
     const int i0 = k * kPrefetch;
-    if (__builtin_expect(careful, false)) {
-      // Rare (a non-finite carry): step by step with exp2_nz, reading delta
-      // and y again, in a compact loop (a second unrolled copy of the block
-      // spilled registers in the common path).
-      float Sr = S_in;  // the same additions as Sj, so the same sums
-#pragma unroll 1
-      for (int j = 0; j < kPrefetch; ++j) {
-        const size_t r = row(i0 + j);
-        Sr += dx(ldv(&at(delta + r, io)));
-        Row<T, NT> Cc;
-        Cc.load(C + (row0 + tof(i0 + j)) * NT);
-        float &yref = at(y + r, yo);
-        yref = yref + fix_step<T, NT, true, true>(Sr, Cc, Ap, cin, live);
-      }
-    } else {
-      Row<T, NT> Cc;
-      Cc.load(C + (row0 + tof(i0)) * NT);
+    Row<T, NT> Cc;
+    Cc.load(C + (row0 + tof(i0)) * NT);
 #pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) {
-        Row<T, NT> Cn;
-        wait_scalar_loads();
-        if (j + 1 < kPrefetch) Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
-        at(y + row(i0 + j), yo) =
-            cur.yv[j] + fix_step<T, NT, true, false>(Sj[j], Cc, Ap, cin, live);
-        if (j + 1 < kPrefetch) Cc = Cn;
-      }
+    for (int j = 0; j < kPrefetch; ++j) {
+      Row<T, NT> Cn;
+      wait_scalar_loads();
+      if (j + 1 < kPrefetch) Cn.load(C + (row0 + tof(i0 + j + 1)) * NT);
+      at(y + row(i0 + j), yo) = yv[j] + fix_step<T, NT, true, false>(Sj[j], Cc, Ap, cin, live);
+      if (j + 1 < kPrefetch) Cc = Cn;
     }
   };
 
@@ -844,26 +854,23 @@ __device__ __forceinline__ void fix_sweep(const T *__restrict__ delta, const T *
     }
     if (masks == 0) continue;  // wave-uniform: the whole window leaves y as it is
     // Its blocks that change y, each one's words loaded while the one before
-    // it computes; two blocks per iteration, so that the two word sets trade
-    // roles without copies.
+    // it computes and taken up after that one's stores, the one way into
+    // that point, so that its waits count those stores and wait for its own
+    // loads alone.
     int i = __builtin_ctz(masks) / 4;
-    Words wa, wb;
-    load_block(w0 + i, wa);
-    auto next_live = [&](uint32_t &live) {
-      live = (masks >> (4 * i)) & 0xfu;
-      masks &= ~(0xfu << (4 * i));
-      return masks ? __builtin_ctz(masks) / 4 : -1;
-    };
+    Words w;
+    float Sj[kPrefetch], yv[kPrefetch];
+    load_block(w0 + i, w);
+    take_up(w, Sj, yv);
     for (;;) {
-      uint32_t live;
-      int inext = next_live(live);
-      run_block(w0 + i, wa, inext >= 0 ? w0 + inext : -1, wb, live);
+      const uint32_t live = (masks >> (4 * i)) & 0xfu;
+      masks &= ~(0xfu << (4 * i));
+      const int inext = masks ? __builtin_ctz(masks) / 4 : -1;
+      if (inext >= 0) load_block(w0 + inext, w);
+      run_block(w0 + i, Sj, yv, live);
       if (inext < 0) break;
       i = inext;
-      inext = next_live(live);
-      run_block(w0 + i, wb, inext >= 0 ? w0 + inext : -1, wa, live);
-      if (inext < 0) break;
-      i = inext;
+      take_up(w, Sj, yv);
     }
   }
   float S = nfull > 0 ? s_end[s0 + size_t(nfull - 1) * ss] : 0.0f;
