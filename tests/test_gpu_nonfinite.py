@@ -193,3 +193,34 @@ def test_nonfinite_s6(case, N, chunk, monkeypatch):
         with np.errstate(all="ignore"):
             ref = oracle.selective_scan(*inp.as_f64(), direction=direction)
         assert_same_nonfinite(y, ref, TOL, f"s6 {case} N={N} {direction}")
+
+
+@pytest.mark.parametrize("chunk", ["256", None])
+@pytest.mark.parametrize("N", [1, 16])
+def test_nonfinite_s6_flush_in_reverse_only(N, chunk, monkeypatch):
+    """L = 3003: the last chunk ends in a tail of 3 steps that the forward
+    sweep takes one step at a time, while the reverse sweep takes them in
+    its first full block of 8. u = +inf at the last step and a huge delta one
+    step before it meet only in the reverse recurrence (an infinite state
+    times an exponential that flushes in fp32), so in the bidirectional call
+    only the reverse sweep has to be evaluated again, after the forward
+    output is formed again. Every output against the float64 oracle."""
+    say(f"nonfinite s6 flush in reverse only N={N} chunk={chunk}")
+    if chunk:
+        monkeypatch.setenv("SSMSCAN_S6_CHUNK", chunk)
+    else:
+        monkeypatch.delenv("SSMSCAN_S6_CHUNK", raising=False)
+    dev = need_gpu()
+    inp = s6_inputs(2, 3003, 64, N, seed=37, dtype="f32")
+    if N == 1:
+        inp.B = torch.ones_like(inp.B)
+        inp.C = torch.ones_like(inp.C)
+        inp.D = torch.zeros_like(inp.D)
+    inp.u[0, 3002, 7] = INF
+    inp.delta[0, 3001, 7] = 200.0
+    t = [x.to(dev) for x in (inp.u, inp.delta, inp.A, inp.B, inp.C, inp.D)]
+    for direction in ("fwd", "rev", "bidir"):
+        y = ssm.selective_scan_fwd(*t, direction=direction).cpu().numpy()
+        with np.errstate(all="ignore"):
+            ref = oracle.selective_scan(*inp.as_f64(), direction=direction)
+        assert_same_nonfinite(y, ref, TOL, f"s6 reverse-only flush N={N} {direction}")
