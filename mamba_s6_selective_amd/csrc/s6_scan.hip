@@ -22,7 +22,7 @@
 //     start) and small per-block statistics for the fix pass.
 //  2. carry pass: per (b, n, d), a left fold over the chunk aggregates gives
 //     each chunk's incoming state (forward and/or reverse); the fold is split
-//     over waves (parts of kCarryPart chunks) joined through LDS.
+//     over waves (parts of 8 or 16 chunks) joined through LDS.
 //  3. fix pass: every chunk except the first (forward) / last (reverse) adds
 //     sum_n C[t,n] * carry_n * exp(A_n * S_t), S_t the running sum of delta
 //     from the carry's entry point, to its y. This is the exact carry
@@ -495,14 +495,17 @@ __global__ __launch_bounds__(kThreads, 4) void s6_chunk_kernel(
 // Per (b, n, d): incoming state of every chunk, by a left fold of the chunk
 // aggregates (forward: chunk 0 upwards; reverse: last chunk down). A block
 // covers 64 channels (lanes) of one (b, n); wave p owns chunks
-// [p*kCarryPart, (p+1)*kCarryPart) in both directions, holds their
-// multipliers and end states in registers, and folds them into part totals;
-// the totals meet in LDS, and each wave then replays its chunks from the fold
-// of the totals before it (forward: lower parts; reverse: higher parts).
-// Fixed shapes, so the result is deterministic.
-constexpr int kCarryPart = 16;
+// [p*Part, (p+1)*Part) in both directions, holds their multipliers and end
+// states in registers, and folds them into part totals; the totals meet in
+// LDS, and each wave then replays its chunks from the fold of the totals
+// before it (forward: lower parts; reverse: higher parts). Part is 8 chunks
+// when that covers the sequence with at most kCarryMaxParts waves, else
+// kCarryPart: short sequences get more, shorter waves (measured faster on
+// 32-chunk sequences). Fixed shapes, so the result is deterministic.
+constexpr int kCarryPart = 16;      // the largest part
 constexpr int kCarryMaxParts = 16;  // so at most 256 chunks
 
+template <int Part>
 __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
     const float *__restrict__ agg_s, const float *__restrict__ agg_f,
     const float *__restrict__ agg_r, const float *__restrict__ A, float *__restrict__ carry_f,
@@ -520,7 +523,7 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
   const int d = dg * 64 + lane;
   const bool valid = d < g.d_inner;
   const bool fwd = direction != SSM_DIR_REV, rev = direction != SSM_DIR_FWD;
-  const int k0 = part * kCarryPart;
+  const int k0 = part * Part;
   // All loads first, from indices clamped into range (lanes past d_inner and
   // chunks past the end read valid entries whose values are then replaced),
   // so that they are in flight together: a load under a per-lane condition
@@ -528,23 +531,23 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
   // time.
   const int dc = valid ? d : 0;
   const float Aval = A[size_t(dc) * NT + n];
-  float ra[kCarryPart], rf[kCarryPart] = {}, rr[kCarryPart] = {};
+  float ra[Part], rf[Part] = {}, rr[Part] = {};
 #pragma unroll
-  for (int i = 0; i < kCarryPart; ++i)
+  for (int i = 0; i < Part; ++i)
     ra[i] = agg_s[sum_index(g, b, min(k0 + i, g.nchunks - 1), dc)];
   if (fwd) {
 #pragma unroll
-    for (int i = 0; i < kCarryPart; ++i)
+    for (int i = 0; i < Part; ++i)
       rf[i] = agg_f[agg_index(g, NT, b, min(k0 + i, g.nchunks - 1), n, dc)];
   }
   if (rev) {
 #pragma unroll
-    for (int i = 0; i < kCarryPart; ++i)
+    for (int i = 0; i < Part; ++i)
       rr[i] = agg_r[agg_index(g, NT, b, min(k0 + i, g.nchunks - 1), n, dc)];
   }
   const float Ap = valid ? Aval * kLog2e : 0.0f;
 #pragma unroll
-  for (int i = 0; i < kCarryPart; ++i) {
+  for (int i = 0; i < Part; ++i) {
     const bool in = valid && k0 + i < g.nchunks;  // chunks past the end act as identity maps
     ra[i] = in ? exp2_nz(Ap * ra[i]) : 1.0f;
     rf[i] = in && fwd ? rf[i] : 0.0f;
@@ -552,9 +555,9 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
   }
   float ta = 1.0f, tf = 0.0f, tr = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kCarryPart; ++i) {
+  for (int i = 0; i < Part; ++i) {
     tf = __builtin_fmaf(ra[i], tf, rf[i]);
-    tr = __builtin_fmaf(ra[kCarryPart - 1 - i], tr, rr[kCarryPart - 1 - i]);
+    tr = __builtin_fmaf(ra[Part - 1 - i], tr, rr[Part - 1 - i]);
     ta = mul_pos_nz(ta, ra[i]);
   }
   s_a[part][lane] = ta;
@@ -565,13 +568,13 @@ __global__ __launch_bounds__(64 * kCarryMaxParts) void s6_carry_kernel(
   for (int q = 0; q < part; ++q) cf = __builtin_fmaf(s_a[q][lane], cf, s_f[q][lane]);
   for (int q = parts - 1; q > part; --q) cr = __builtin_fmaf(s_a[q][lane], cr, s_r[q][lane]);
 #pragma unroll
-  for (int i = 0; i < kCarryPart; ++i) {
+  for (int i = 0; i < Part; ++i) {
     const int k = k0 + i;
     if (fwd && valid && k < g.nchunks) carry_f[agg_index(g, NT, b, k, n, d)] = cf;
     cf = __builtin_fmaf(ra[i], cf, rf[i]);
   }
 #pragma unroll
-  for (int i = kCarryPart - 1; i >= 0; --i) {
+  for (int i = Part - 1; i >= 0; --i) {
     const int k = k0 + i;
     if (rev && valid && k < g.nchunks) carry_r[agg_index(g, NT, b, k, n, d)] = cr;
     cr = __builtin_fmaf(ra[i], cr, rr[i]);
@@ -1056,10 +1059,16 @@ int launch_all(const S6Args &a, hipStream_t stream) {
                      sf_min, sr_end, sr_min, g, a.direction);
   if (int rc = hip_check(hipGetLastError(), "s6 chunk launch")) return rc;
   if (g.nchunks == 1) return SSM_OK;
-  const int parts = (g.nchunks + kCarryPart - 1) / kCarryPart;
   const int64_t carry_blocks = int64_t(a.batch) * NT * ((a.d_inner + 63) / 64);
-  hipLaunchKernelGGL(s6_carry_kernel, dim3(unsigned(carry_blocks)), dim3(64 * parts), 0, stream,
-                     agg_s, agg_f, agg_r, a.A, car_f, car_r, g, NT, a.direction);
+  auto carry = [&](auto kernel, int part) {
+    const int parts = (g.nchunks + part - 1) / part;
+    hipLaunchKernelGGL(kernel, dim3(unsigned(carry_blocks)), dim3(64 * parts), 0, stream, agg_s,
+                       agg_f, agg_r, a.A, car_f, car_r, g, NT, a.direction);
+  };
+  if (g.nchunks <= 8 * kCarryMaxParts)
+    carry(s6_carry_kernel<8>, 8);
+  else
+    carry(s6_carry_kernel<kCarryPart>, kCarryPart);
   if (int rc = hip_check(hipGetLastError(), "s6 carry launch")) return rc;
   hipLaunchKernelGGL((s6_fix_kernel<T, NT, DX>), dim3(unsigned(wgs)), dim3(kThreads), 0, stream,
                      u, dl, a.delta_bias, a.A, B, C, a.D, a.y, car_f, car_r, sf_end, sf_min,
