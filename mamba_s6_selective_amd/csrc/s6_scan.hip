@@ -972,12 +972,15 @@ __global__ __launch_bounds__(kThreads, 4) void s6_fix_kernel(
   }
 }
 
-// Chunk length (a multiple of 8): as many (batch, chunk, channel-group)
-// workgroups as the GPU holds at once (one round, so every workgroup starts
-// together and none waits for a second round), chunks of at least 32 steps
-// (shorter ones leave the carry no room to decay, so the fix pass redoes
-// nearly all the work: 16-step chunks measured 4 % slower on a 1024-step
-// sequence), at most kCarryPart * kCarryMaxParts chunks per sequence.
+// Chunk length (a multiple of 8): the largest power-of-two number of chunks
+// per sequence whose (batch, chunk, channel-group) workgroups the GPU holds
+// at once (one round, so every workgroup starts together and none waits for
+// a second round), chunks of at least 32 steps (shorter ones leave the carry
+// no room to decay, so the fix pass redoes nearly all the work: 16-step
+// chunks measured 10 % slower on a 1024-step sequence), at most
+// kCarryPart * kCarryMaxParts chunks per sequence. Filling every resident
+// slot instead measured 2-6 % slower on each of the four shapes tried where
+// the two differ: every chunk boundary adds fix-pass work.
 // SSMSCAN_S6_CHUNK overrides the length (still within the chunk-count limit).
 int plan_chunk(int batch, int L, int groups, int resident_wgs) {
   const int64_t max_chunks = kCarryPart * kCarryMaxParts;
@@ -985,8 +988,9 @@ int plan_chunk(int batch, int L, int groups, int resident_wgs) {
   if (const char *env = getenv("SSMSCAN_S6_CHUNK")) chunk = atoi(env);
   if (chunk <= 0) {
     const int64_t rows = int64_t(batch) * groups;
-    int64_t nch = resident_wgs / rows;
-    if (nch < 1) nch = 1;
+    const int64_t fit = resident_wgs / rows;
+    int64_t nch = 1;
+    while (2 * nch <= fit) nch *= 2;
     chunk = (L + nch - 1) / nch;
     if (chunk < 32) chunk = 32;
   }
