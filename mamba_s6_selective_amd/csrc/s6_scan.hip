@@ -254,7 +254,7 @@ struct SweepStats {
 
 // One sweep of the chunk-local recurrence from a zero state. Writes (or, when
 // Accumulate, adds) y for every step of the chunk, the block statistics in
-// st (when st.word is set), and leaves the final state in h and the sum of
+// st (when st.s_min is set), and leaves the final state in h and the sum of
 // delta in S. Steps run in blocks of kPrefetch with no
 // branch inside a block (so the compiler can overlap neighbouring steps), and
 // each lane's words for the next block are loaded while the current block
